@@ -1,0 +1,177 @@
+"""Python binding of the gfx950 affine group-quantized matrix product library.
+
+Thin argument marshalling over the C ABI of ``include/qmm.h`` (``libqmm.so``
+built in this directory): the functions below carry the C names, check
+tensor dtypes/devices/shapes, pass device pointers and torch's current HIP
+stream, and turn negative return codes into exceptions. Every step of the
+product runs in the library's HIP kernels; there is no fallback path.
+
+Tensors (all on one ROCm device, contiguous):
+  x       float16 [M, K]
+  wq      int32 or uint32 [N, K*bits/32]   (bit patterns of the packed words)
+  scales  float16 [N, K/G]
+  biases  float16 [N, K/G]
+  y       float32 [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIBRARY_PATH = Path(__file__).resolve().parent / "libqmm.so"
+
+if not LIBRARY_PATH.exists():
+    raise ImportError(
+        f"{LIBRARY_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()' at the repository root)")
+
+_lib = ctypes.CDLL(str(LIBRARY_PATH))
+
+_p, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_lib.qmm_pack.argtypes = [_p, _p, _i, _i, _i, _p]
+_lib.qmm_forward.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
+_lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.qmm_splitk_workspace_bytes.restype = _sz
+_lib.qmm_validate.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz]
+_lib.qmm_strerror.argtypes = [_i]
+_lib.qmm_strerror.restype = ctypes.c_char_p
+_lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
+_lib.qmm_kernel_name.restype = ctypes.c_char_p
+for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_splitk, _lib.qmm_forward_kernel,
+           _lib.qmm_validate):
+    _f.restype = _i
+
+EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_splitk", "qmm_splitk_workspace_bytes",
+            "qmm_validate", "qmm_strerror", "qmm_kernel_name", "qmm_forward_kernel")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {qmm_strerror(code)} (code {code})")
+        self.code = code
+
+
+def qmm_strerror(code: int) -> str:
+    return _lib.qmm_strerror(code).decode()
+
+
+def qmm_splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:
+    return int(_lib.qmm_splitk_workspace_bytes(M, N, split_k))
+
+
+def qmm_kernel_name(M: int, K: int, N: int, bits: int, G: int) -> str | None:
+    name = _lib.qmm_kernel_name(M, K, N, bits, G)
+    return name.decode() if name else None
+
+
+def qmm_validate(x_ptr: int, wq_ptr: int, s_ptr: int, b_ptr: int, y_ptr: int, M: int, K: int,
+                 N: int, bits: int, G: int, split_k: int = 0, ws_ptr: int = 0,
+                 ws_bytes: int = 0) -> int:
+    """Host-only argument validation on raw addresses (no GPU needed)."""
+    return int(_lib.qmm_validate(x_ptr or None, wq_ptr or None, s_ptr or None, b_ptr or None,
+                                 y_ptr or None, M, K, N, bits, G, split_k, ws_ptr or None,
+                                 ws_bytes))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU device {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_WORD_DTYPES = (torch.int32, torch.uint32)
+
+
+def _operands(x, wq, scales, biases, bits, G):
+    if x.dim() != 2 or wq.dim() != 2:
+        raise ValueError("x and wq must be 2-D")
+    M, K = x.shape
+    N = wq.shape[0]
+    if K % G or (K * bits) % 32:
+        raise ValueError("K must be a multiple of G (and K*bits of 32)")
+    dev = x.device
+    _check(x, "x", (torch.float16,), (M, K), None)
+    _check(wq, "wq", _WORD_DTYPES, (N, K * bits // 32), dev)
+    _check(scales, "scales", (torch.float16,), (N, K // G), dev)
+    _check(biases, "biases", (torch.float16,), (N, K // G), dev)
+    return M, K, N, dev
+
+
+def qmm_pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack uint8 codes [N, K] into int32 words [N, K*bits/32] on the GPU."""
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D")
+    N, K = codes.shape
+    _check(codes, "codes", (torch.uint8,), (N, K), None)
+    if (K * bits) % 32:
+        raise ValueError("K*bits must be a multiple of 32")
+    if out is None:
+        out = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
+    _check(out, "out", _WORD_DTYPES, (N, K * bits // 32), codes.device)
+    rc = _lib.qmm_pack(codes.data_ptr(), out.data_ptr(), N, K, bits, _stream(codes))
+    if rc:
+        raise QmmError(rc, "qmm_pack")
+    return out
+
+
+def qmm_forward(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Tensor:
+    """y = x . W^T (fp32 [M, N]) for packed affine weights."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    rc = _lib.qmm_forward(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                          out.data_ptr(), M, K, N, bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward")
+    return out
+
+
+def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,
+                       out=None) -> torch.Tensor:
+    """qmm_forward with an explicitly named kernel ("qmv" or "mfma")."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    rc = _lib.qmm_forward_kernel(kernel.encode(), x.data_ptr(), wq.data_ptr(),
+                                 scales.data_ptr(), biases.data_ptr(), out.data_ptr(), M, K, N,
+                                 bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_kernel")
+    return out
+
+
+def qmm_forward_splitk(x, wq, scales, biases, bits: int, G: int, split_k: int,
+                       workspace=None, out=None) -> torch.Tensor:
+    """The product with K split into split_k slices and an in-order fp32 reduction."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    need = qmm_splitk_workspace_bytes(M, N, split_k)
+    if workspace is None and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = _lib.qmm_forward_splitk(x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+                                 biases.data_ptr(), out.data_ptr(), M, K, N, bits, G, split_k,
+                                 ws_ptr, ws_bytes, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_splitk")
+    return out

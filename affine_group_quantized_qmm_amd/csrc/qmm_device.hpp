@@ -1,0 +1,195 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// the in-register code unpack/widen path, the activation permutation that
+// matches it, and wavefront reductions.
+//
+// The unpack follows the factored evaluation of the vmlx-swift pull request
+// #565 page, commit "LaneQMM": raw b-bit codes are widened to exact fp16
+// integers and multiplied with the activations; the scale and bias are
+// applied to the group's dot product afterwards (C += s*P + b*XS). The same
+// page's qwen_mixed_qmv commit attributes a compute-bound one-row mat-vec to
+// inner loops with run-time bounds that cannot unroll; every loop bound and
+// bit offset here is a compile-time constant of (bits, G).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace qmm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---------------------------------------------------------------------------
+// Pairing of codes into fp16 pairs.
+//
+// A 32-bit window of the bitstream holds two codes, one in each 16-bit half,
+// each entirely inside the half's 10 fraction bits at offset o (o + bits <= 10).
+// OR-ing the exponent of 2^(10-o) into that half turns the bits into the fp16
+// number 2^(10-o) + code exactly; subtracting 2^(10-o) then leaves the code
+// as an exact fp16 integer. One window, one mask-or and one packed subtract
+// give two codes.
+//
+// Codes are paired (i, i+d) inside blocks of 2d consecutive codes, with d
+// chosen per width so that code i+d always lands in the upper half of a
+// window whose lower half holds code i:
+//   bits 4: d = 4 (16 bits apart)   bits 5: d = 4 (20 bits apart)
+//   bits 6: d = 2 (12 bits apart)   bits 8: d = 2 (16 bits apart)
+// Pair P of a run of codes therefore holds codes lo(P) and lo(P) + d, and
+// the activations are stored in the same pair order ("permuted order").
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int pair_dist(int bits) { return (bits == 4 || bits == 5) ? 4 : 2; }
+
+// Index (within a run of codes starting at a block boundary) of the lower
+// code of pair P, and of the code at permuted position `pos`.
+__host__ __device__ constexpr int pair_lo(int bits, int P)
+{
+    return 2 * pair_dist(bits) * (P / pair_dist(bits)) + P % pair_dist(bits);
+}
+__host__ __device__ constexpr int perm_code(int bits, int pos)
+{
+    return pair_lo(bits, pos / 2) + ((pos & 1) ? pair_dist(bits) : 0);
+}
+
+// Offset of the lower code inside the lower half: within the allowed range,
+// prefer one that puts the window start on a byte boundary.
+__host__ __device__ constexpr int pair_lo_offset(int bits, int p_lo)
+{
+    const int D = bits * pair_dist(bits) - 16;      // o_hi - o_lo
+    const int lo_min = D < 0 ? -D : 0;
+    const int lo_max = (10 - bits) - (D > 0 ? D : 0);
+    for (int o = lo_min; o <= lo_max; ++o)
+        if (((p_lo - o) % 8 + 8) % 8 == 0)
+            return o;
+    return lo_min;
+}
+
+__host__ __device__ constexpr uint32_t half_pow2_bits(int e) { return (uint32_t)(15 + e) << 10; }
+
+// 32-bit window of the stream starting at bit S (S may be negative: the
+// bits below 0 read as zero). The words hold the stream from bit 0.
+template <int S, int NW>
+__device__ __forceinline__ uint32_t stream_window(const uint32_t (&w)[NW])
+{
+    if constexpr (S < 0) {
+        return w[0] << (-S);
+    } else {
+        constexpr int j = S / 32, r = S % 32;
+        static_assert(j < NW, "window starts past the loaded words");
+        if constexpr (r == 0)
+            return w[j];
+        else if constexpr (j + 1 < NW)
+            return __builtin_amdgcn_alignbit(w[j + 1], w[j], r);
+        else
+            return w[j] >> r;
+    }
+}
+
+// fp16 pair (code lo(P), code lo(P)+d) of a run of codes stored from bit 0 of w.
+template <int BITS, int P, int NW>
+__device__ __forceinline__ half2_t code_pair(const uint32_t (&w)[NW])
+{
+    constexpr int d = pair_dist(BITS);
+    constexpr int i = pair_lo(BITS, P);
+    constexpr int p_lo = BITS * i;
+    constexpr int o_lo = pair_lo_offset(BITS, p_lo);
+    constexpr int o_hi = o_lo + BITS * d - 16;
+    static_assert(o_lo >= 0 && o_lo + BITS <= 10, "low code does not fit the fraction");
+    static_assert(o_hi >= 0 && o_hi + BITS <= 10, "high code does not fit the fraction");
+    static_assert(BITS * (i + d) + BITS <= 32 * NW, "pair reads past the loaded words");
+    constexpr uint32_t code_mask = (1u << BITS) - 1u;
+    constexpr uint32_t mask = (code_mask << o_lo) | (code_mask << (16 + o_hi));
+    constexpr uint32_t magic = half_pow2_bits(10 - o_lo) | (half_pow2_bits(10 - o_hi) << 16);
+    const uint32_t win = stream_window<p_lo - o_lo>(w);
+    const half2_t v = __builtin_bit_cast(half2_t, (win & mask) | magic);
+    const half2_t off = {(_Float16)(float)(1 << (10 - o_lo)), (_Float16)(float)(1 << (10 - o_hi))};
+    return v - off;
+}
+
+template <int BITS, int NW, int... Ps>
+__device__ __forceinline__ void unpack_pairs_impl(const uint32_t (&w)[NW], half2_t *out,
+                                                  std::integer_sequence<int, Ps...>)
+{
+    ((out[Ps] = code_pair<BITS, Ps>(w)), ...);
+}
+
+// Widen NCODES codes (stored from bit 0 of w) into NCODES/2 fp16 pairs in
+// pair order.
+template <int BITS, int NCODES, int NW>
+__device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&out)[NCODES / 2])
+{
+    static_assert(NCODES % (2 * pair_dist(BITS)) == 0, "runs must hold whole pairing blocks");
+    unpack_pairs_impl<BITS, NW>(w, out, std::make_integer_sequence<int, NCODES / 2>{});
+}
+
+// ---------------------------------------------------------------------------
+// Loads of NW consecutive words with a known byte alignment.
+// ---------------------------------------------------------------------------
+template <int NW, int ALIGN>
+__device__ __forceinline__ void load_words(const uint32_t *__restrict__ p, uint32_t (&w)[NW])
+{
+    if constexpr (ALIGN >= 16 && NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+            w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (ALIGN >= 8 && NW % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 2; ++i) {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p) + i);
+            w[2 * i + 0] = v.x; w[2 * i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            w[i] = __builtin_nontemporal_load(p + i);
+    }
+}
+
+__host__ __device__ constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// ---------------------------------------------------------------------------
+// Wavefront (64-lane) reductions.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x124>(v);  // row_ror:4
+    v += dpp_f32<0x128>(v);  // row_ror:8
+    return v;
+}
+
+// Sum over all 64 lanes, returned to every lane (a wave-uniform value).
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row16_sum(v);
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+}  // namespace qmm

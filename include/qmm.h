@@ -1,0 +1,156 @@
+/*
+ * qmm.h - affine group-quantized matrix product for AMD Instinct MI355X (gfx950).
+ *
+ * Computes y[M,N] = x[M,K] . W[N,K]^T where W is stored as packed b-bit
+ * unsigned codes q with one fp16 scale s and one fp16 bias b per group of G
+ * consecutive codes along K:
+ *
+ *     W[n,k] = s[n, k/G] * q[n,k] + b[n, k/G]
+ *
+ * The library never forms W. It evaluates the factored form
+ *
+ *     y[m,n] = sum over groups g of  s[n,g] * P[m,n,g] + b[n,g] * XS[m,g]
+ *     P[m,n,g] = sum_{k in g} q[n,k] * x[m,k],   XS[m,g] = sum_{k in g} x[m,k]
+ *
+ * with the dequantization applied after the dot product, as described in the
+ * vmlx-swift pull request #565 page, commit "LaneQMM" (tensor-op matmul over
+ * raw affine codes, C += s*P + b*XS, 5/6/8-bit codes widened on the GPU).
+ * Products of exact fp16 codes and fp16 activations are accumulated in fp32;
+ * the result is fp32 (the same page's "batched GDN tail" commit notes the
+ * float32 promotion of batched quantized-matmul output).
+ *
+ * Data layout (all row-major, all device memory):
+ *   x       fp16 [M, K]            IEEE binary16 bit patterns (uint16_t)
+ *   wq      uint32 [N, K*bits/32]  row n holds one least-significant-bit-
+ *                                  first bitstream of K codes: code k occupies
+ *                                  stream bits k*bits .. k*bits+bits-1, stream
+ *                                  bit t is bit (t mod 32) of word t/32.
+ *   scales  fp16 [N, K/G]
+ *   biases  fp16 [N, K/G]
+ *   y       fp32 [M, N]            overwritten, never accumulated into
+ *
+ * Supported: bits in {4, 5, 6, 8} (the formats consumed as stored in the
+ * "Qwen3.8 Flash Next performance and parity receipt" page, section
+ * "MTPLX logic review", plus the 5/6-bit widths of the "LaneQMM" commit);
+ * G in {32, 64, 128}; K a positive multiple of G; N >= 1; M >= 1 (tuned for
+ * M = 1..16 verify rows; larger M is processed 16 rows at a time).
+ *
+ * Ownership: the caller owns every buffer. Functions without a workspace
+ * argument need no scratch memory; no entry point allocates device memory.
+ * Work is enqueued on the caller's stream and the call returns without
+ * waiting; results are visible after the stream is synchronized.
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * GPU work and returns 0 on success or one of the negative codes below.
+ * Argument errors launch nothing. A launch failure reported by the HIP
+ * runtime returns QMM_ERR_LAUNCH; execution faults surface at stream
+ * synchronization as with any HIP kernel. No exception or abort crosses
+ * this interface. The library is stateless and may be called from several
+ * host threads at once.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMM_OK 0
+#define QMM_ERR_NULL (-1)          /* a required pointer is NULL */
+#define QMM_ERR_SHAPE (-2)         /* M < 1, K < 1, N < 1, K % G != 0 or a size overflows */
+#define QMM_ERR_BITS (-3)          /* bits not in {4, 5, 6, 8} */
+#define QMM_ERR_GROUP (-4)         /* G not in {32, 64, 128} */
+#define QMM_ERR_SPLIT (-5)         /* split_k < 1 or split_k > K/G */
+#define QMM_ERR_WORKSPACE (-6)     /* workspace smaller than qmm_splitk_workspace_bytes */
+#define QMM_ERR_ALIGN (-7)         /* x, wq, scales, biases, y or workspace not 16-byte aligned */
+#define QMM_ERR_LAUNCH (-8)        /* the HIP runtime rejected a kernel launch */
+
+/*
+ * qmm_pack - pack unpacked codes into the bitstream layout above.
+ *
+ * codes  [N, K] uint8, device memory; only the low `bits` bits of each byte
+ *        are stored (higher bits are ignored).
+ * packed [N, K*bits/32] uint32, device memory, written in full.
+ * Requires K*bits to be a multiple of 32 (true whenever 32 divides K).
+ * Packing is offline work (weights are packed once and then consumed as
+ * stored); it is bit-exact with respect to the layout definition.
+ */
+int qmm_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,
+             hipStream_t stream);
+
+/*
+ * qmm_forward - y = x . W^T for the packed affine weights (one call, one
+ * or more kernel launches on `stream`, no scratch memory).
+ *
+ * x [M,K] fp16, wq [N, K*bits/32] uint32, scales/biases [N, K/G] fp16,
+ * y [M,N] fp32; all device pointers, 16-byte aligned.
+ * The kernel is chosen on the host from (M, bits, G, K, N): a
+ * one-row mat-vec for M = 1 and a multi-row kernel that streams the
+ * weights once for all rows otherwise (the vmlx-swift pull request #565
+ * page, tiling-policy commit, routes fewer than four rows to the
+ * one-row mat-vec because it is faster there).
+ */
+int qmm_forward(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
+                hipStream_t stream);
+
+/*
+ * qmm_forward_splitk - the same product with K divided into split_k slices.
+ *
+ * Slices are whole groups: with Kg = K/G groups, slice z covers
+ * floor(Kg/split_k) groups plus one more for z < Kg mod split_k, in
+ * ascending order. A first kernel writes slice z's fp32 partial product to
+ * workspace[z][M][N]; a second kernel sums the split_k partials in order
+ * z = 0 .. split_k-1 into y. There are no atomics: reruns are bitwise
+ * identical. The summation order differs from qmm_forward, so the two
+ * agree within the fp32 tolerance, not bitwise. This follows the split-K
+ * verify tile of the vmlx-swift pull request #565 page (JANGH dense verify
+ * split-K commit: K sliced across the grid, fp32 partials summed after).
+ *
+ * 1 <= split_k <= K/G. workspace: device memory of at least
+ * qmm_splitk_workspace_bytes(M, N, split_k) bytes, 16-byte aligned, owned by
+ * the caller; its contents on entry do not matter and are overwritten.
+ * With split_k == 1 the product is written to y directly, no workspace is
+ * needed and `workspace` may be NULL.
+ */
+int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                       const uint16_t *biases, float *y, int M, int K, int N, int bits,
+                       int G, int split_k, float *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of workspace qmm_forward_splitk needs: split_k * M * N * 4 for
+ * split_k >= 2, 0 for split_k == 1 and for invalid arguments. */
+size_t qmm_splitk_workspace_bytes(int M, int N, int split_k);
+
+/* Host-only validation of qmm_forward / qmm_forward_splitk arguments
+ * (split_k = 0 validates a qmm_forward call). Returns the code the entry
+ * point would return before launching anything. Touches no GPU state. */
+int qmm_validate(const void *x, const void *wq, const void *scales, const void *biases,
+                 const void *y, int M, int K, int N, int bits, int G, int split_k,
+                 const void *workspace, size_t workspace_bytes);
+
+/* Static description of an error code (never NULL). */
+const char *qmm_strerror(int code);
+
+/* Name of the kernel qmm_forward would launch for these arguments
+ * ("qmv" or "mfma") or NULL for invalid ones. Host-only. */
+const char *qmm_kernel_name(int M, int K, int N, int bits, int G);
+
+/* qmm_forward with the kernel named explicitly instead of chosen from M
+ * (a test and benchmark aid): "qmv" runs the one-row mat-vec once per
+ * activation row (streaming the weights M times), "mfma" runs the multi-row
+ * kernel. Same arguments, layout and errors as qmm_forward; an unknown name
+ * returns QMM_ERR_SHAPE, a NULL name QMM_ERR_NULL. */
+int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,
+                       const uint16_t *scales, const uint16_t *biases, float *y, int M,
+                       int K, int N, int bits, int G, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

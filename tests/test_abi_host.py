@@ -1,0 +1,83 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/qmm.h declares, and rejects bad arguments with the
+documented codes before touching the GPU."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "qmm.h"
+
+qmm = pytest.importorskip("affine_group_quantized_qmm_amd",
+                          reason="libqmm.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qmm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("qmm_pack", "qmm_forward", "qmm_forward_splitk"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(str(qmm.LIBRARY_PATH))
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(declared_functions()) == set(qmm.EXPORTED)
+
+
+def test_error_codes_and_messages():
+    for code in range(0, -9, -1):
+        assert qmm.qmm_strerror(code) and "unknown" not in qmm.qmm_strerror(code)
+    assert "unknown" in qmm.qmm_strerror(-99)
+
+
+A = 0x10000  # a fake, 16-byte aligned address: validation never dereferences it
+
+
+def v(**kw):
+    args = dict(x=A, wq=A, s=A, b=A, y=A, M=4, K=512, N=256, bits=4, G=32, split=0, ws=0, wsb=0)
+    args.update(kw)
+    return qmm.qmm_validate(args["x"], args["wq"], args["s"], args["b"], args["y"], args["M"],
+                            args["K"], args["N"], args["bits"], args["G"], args["split"],
+                            args["ws"], args["wsb"])
+
+
+def test_validation_accepts_good_arguments():
+    assert v() == 0
+    for bits in (4, 5, 6, 8):
+        for G in (32, 64, 128):
+            assert v(bits=bits, G=G, K=G * 3) == 0
+    need = qmm.qmm_splitk_workspace_bytes(4, 256, 3)
+    assert need == 3 * 4 * 256 * 4
+    assert v(split=3, ws=A, wsb=need) == 0
+    assert v(split=1) == 0  # no workspace needed for one slice
+    assert qmm.qmm_splitk_workspace_bytes(4, 256, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), -1), (dict(wq=0), -1), (dict(s=0), -1), (dict(b=0), -1), (dict(y=0), -1),
+    (dict(split=2, ws=0, wsb=1 << 20), -1),
+    (dict(M=0), -2), (dict(K=0), -2), (dict(N=0), -2), (dict(K=100), -2), (dict(K=48, G=32), -2),
+    (dict(N=-5), -2), (dict(K=1 << 29), -2),
+    (dict(bits=3), -3), (dict(bits=7), -3), (dict(bits=16), -3),
+    (dict(G=16), -4), (dict(G=96), -4),
+    (dict(split=-1, ws=A, wsb=1 << 30), -5), (dict(split=17, ws=A, wsb=1 << 30), -5),
+    (dict(split=2, ws=A, wsb=100), -6),
+    (dict(x=A + 2), -7), (dict(wq=A + 4), -7), (dict(y=A + 8), -7), (dict(s=A + 2), -7),
+    (dict(split=2, ws=A + 4, wsb=1 << 20), -7),
+])
+def test_validation_rejects(kw, code):
+    assert v(**kw) == code
+
+
+def test_kernel_choice():
+    assert qmm.qmm_kernel_name(1, 5120, 17408, 4, 32) == "qmv"
+    assert qmm.qmm_kernel_name(16, 5120, 17408, 4, 32) == "mfma"
+    assert qmm.qmm_kernel_name(16, 5120, 17408, 3, 32) is None
