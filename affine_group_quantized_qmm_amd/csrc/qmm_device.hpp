@@ -117,15 +117,57 @@ __device__ __forceinline__ half2_t code_pair(const uint32_t (&w)[NW])
     return v - off;
 }
 
+// v_and_or_b32 (x & mask) | magic. The compiler does not fuse the two
+// operations when both constants are literals, so it is written out.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+    return r;
+}
+
+// 4-bit codes take a cheaper route: all codes of a word are moved to bits
+// 4..7 of their half (the high nibble of each byte pair needs no shift, the
+// others one shift each) and become 64 + code with one v_and_or_b32. The
+// constant 64 is not subtracted per code: since every code carries it,
+// sum_k (64 + q_k) x_k = P + 64 XS, and the epilogue folds 64*s*XS into the
+// bias (b' = b - 64 s). Three shifts and four v_and_or_b32 per word.
+template <int P>
+__device__ __forceinline__ half2_t code_pair4_offset64(uint32_t word)
+{
+    constexpr uint32_t mask = 0x00F000F0u;          // bits 4..7 of each half
+    constexpr uint32_t magic = 0x54005400u;         // 2^6 in each half
+    uint32_t v;
+    if constexpr (P == 0)
+        v = word << 4;
+    else if constexpr (P == 1)
+        v = word;
+    else if constexpr (P == 2)
+        v = word >> 4;
+    else
+        v = word >> 8;
+    return __builtin_bit_cast(half2_t, and_or(v, mask, magic));
+}
+
+// Offset every widened code carries (see code_pair4_offset64): the epilogue
+// uses s * (P' - kCodeOffset * XS) = s * P.
+template <int BITS>
+struct CodeOffset {
+    static constexpr float value = BITS == 4 ? 64.0f : 0.0f;
+};
+
 template <int BITS, int NW, int... Ps>
 __device__ __forceinline__ void unpack_pairs_impl(const uint32_t (&w)[NW], half2_t *out,
                                                   std::integer_sequence<int, Ps...>)
 {
-    ((out[Ps] = code_pair<BITS, Ps>(w)), ...);
+    if constexpr (BITS == 4)
+        ((out[Ps] = code_pair4_offset64<Ps % 4>(w[Ps / 4])), ...);
+    else
+        ((out[Ps] = code_pair<BITS, Ps>(w)), ...);
 }
 
 // Widen NCODES codes (stored from bit 0 of w) into NCODES/2 fp16 pairs in
-// pair order.
+// pair order: exact integers for 5, 6 and 8 bits, 64 + code for 4 bits.
 template <int BITS, int NCODES, int NW>
 __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&out)[NCODES / 2])
 {
@@ -134,31 +176,64 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&
 }
 
 // ---------------------------------------------------------------------------
-// Loads of NW consecutive words with a known byte alignment.
+// Loads of NW consecutive words with a known byte alignment. Packed weights
+// are read once per call, so the loads carry the non-temporal hint unless
+// QMM_WEIGHT_LOADS_NT is defined to 0.
 // ---------------------------------------------------------------------------
+#ifndef QMM_WEIGHT_LOADS_NT
+#define QMM_WEIGHT_LOADS_NT 1
+#endif
+
+template <typename T>
+__device__ __forceinline__ T load_weight(const T *p)
+{
+#if QMM_WEIGHT_LOADS_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
 template <int NW, int ALIGN>
 __device__ __forceinline__ void load_words(const uint32_t *__restrict__ p, uint32_t (&w)[NW])
 {
     if constexpr (ALIGN >= 16 && NW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+            const u32x4 v = load_weight(reinterpret_cast<const u32x4 *>(p) + i);
             w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
     } else if constexpr (ALIGN >= 8 && NW % 2 == 0) {
 #pragma unroll
         for (int i = 0; i < NW / 2; ++i) {
-            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p) + i);
+            const u32x2 v = load_weight(reinterpret_cast<const u32x2 *>(p) + i);
             w[2 * i + 0] = v.x; w[2 * i + 1] = v.y;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < NW; ++i)
-            w[i] = __builtin_nontemporal_load(p + i);
+            w[i] = load_weight(p + i);
     }
 }
 
 __host__ __device__ constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// Empty asm that claims to modify v: nothing computed from v can be moved
+// above this point. Used where a register stage is consumed, so that work on
+// loads still in flight is not hoisted (which would force an early wait).
+template <typename T>
+__device__ __forceinline__ void pin_register(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
+// base + a 32-bit byte offset: with a wave-uniform base this maps onto the
+// scalar-base + 32-bit vector-offset addressing of global loads.
+template <typename T>
+__device__ __forceinline__ const T *byte_offset(const T *base, uint32_t bytes)
+{
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + bytes);
+}
 
 // ---------------------------------------------------------------------------
 // Wavefront (64-lane) reductions.

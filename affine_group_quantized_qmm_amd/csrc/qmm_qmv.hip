@@ -16,7 +16,10 @@
 //    activations are staged, overlapping that latency;
 //  * the activations of a K chunk are staged once per workgroup in LDS with
 //    16-byte loads, permuted to the pair order of the code unpack, together
-//    with their per-group sums XS;
+//    with their per-group sums XS, and so are the scales and biases of the
+//    workgroup's rows (16-byte loads, one (scale, bias) pair per LDS word);
+//    these loads are issued before the weight prefetch so that they head the
+//    memory queue;
 //  * a group's codes are widened to exact fp16 pairs in registers and dotted
 //    with v_dot2 (fp32 accumulation), then s*P + b*XS is added;
 //  * each wave sums its lanes per row with DPP row rotations and readlanes.
@@ -29,6 +32,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerWave = 4;
+constexpr int kPrefetchRows = 1;  // rows of loads kept in flight per wave
 constexpr int kMaxChunkK = 8192;  // activations staged per pass: at most 16 KB of fp16
 
 // The 8 activations of an aligned 8-code run in the unpack's pair order.
@@ -41,7 +45,7 @@ __device__ __forceinline__ half8_t to_pair_order8(half8_t v)
         return __builtin_shufflevector(v, v, 0, 2, 1, 3, 4, 6, 5, 7);
 }
 
-template <int BITS, int G, int SLOTS, int RPW>
+template <int BITS, int G, int SLOTS, int RPW, int PD_ROWS>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
     constexpr int NWG = G * BITS / 32;        // words per group
@@ -50,22 +54,34 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     constexpr int CHUNK_G = SLOTS * kWave;    // groups per staged chunk
     constexpr int ALIGN = gcd_int(4 * NWG, 16);
     constexpr int TASKS = RPW * SLOTS;
-    constexpr int PD = TASKS < 2 * SLOTS ? TASKS : 2 * SLOTS;  // tasks in flight
+    constexpr int PD = TASKS < PD_ROWS * SLOTS ? TASKS : PD_ROWS * SLOTS;  // tasks in flight
+    constexpr int ROWS = kWaves * RPW;        // rows of the workgroup
+    constexpr int XUNITS = CHUNK_G * UPG;                           // activation units per chunk
+    constexpr int XPT = (XUNITS + kThreads - 1) / kThreads;         // ... per thread
+    constexpr int SBU = ROWS * CHUNK_G / 8;                         // 8-group scale units per chunk
+    constexpr int SPT = (SBU + kThreads - 1) / kThreads;            // ... per thread
     static_assert(CHUNK_G * G <= kMaxChunkK, "staged chunk too large");
+    static_assert(CHUNK_G % 8 == 0, "chunks hold whole 8-group scale units");
 
-    __shared__ half8_t xp[CHUNK_G * UPG];
+    // Activations unit-major: xp[u][g] holds units u of group g, so the
+    // 64 lanes of a wave (consecutive groups) read consecutive 16-byte units.
+    __shared__ half8_t xp[UPG][CHUNK_G];
     __shared__ float xsum[CHUNK_G];
+    __shared__ uint32_t sbl[ROWS][CHUNK_G];   // (scale, bias) fp16 pair per row and group
 
     const int K = a.K, N = a.N, Kg = K / G;
     const size_t wpr = (size_t)K * BITS / 32;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int row0 = (blockIdx.x * kWaves + wave) * RPW;
+    const int wg_row0 = blockIdx.x * ROWS;
+    const int row0 = wg_row0 + wave * RPW;
 
     int gbeg = 0, gend = Kg;
     if (a.split > 1)
         slice_groups(Kg, a.split, blockIdx.z, gbeg, gend);
     float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
+    // 16-byte scale/bias staging needs 8-group alignment of every row span
+    const bool sb_vector = Kg % 8 == 0 && gbeg % 8 == 0 && gend % 8 == 0;
 
     // Row of each task (clamped so loads stay in bounds; results of rows >= N are dropped).
     size_t rowoff[RPW];
@@ -78,52 +94,110 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     for (int r = 0; r < RPW; ++r)
         acc[r] = 0.f;
 
-    // Scale and bias stay raw 16-bit values until they are used, so nothing
-    // consumes a load right after it is issued.
     struct Stage {
         uint32_t w[NWG];
-        uint16_t s, b;
     };
     Stage ring[PD];
 
     for (int g0 = gbeg; g0 < gend; g0 += CHUNK_G) {
         const int ng = min(CHUNK_G, gend - g0);
 
-        // Every load is unconditional (lanes past the chunk re-read its last
-        // group), so the compiler can keep the ring of stages in flight.
+        // 1. Activation and scale/bias loads first: they head the memory
+        //    queue, so the workgroup can start computing as early as possible.
+        half8_t xreg[XPT];
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int u = min((int)threadIdx.x + t * kThreads, ng * UPG - 1);
+            xreg[t] = *reinterpret_cast<const half8_t *>(a.x + (size_t)g0 * G + 8 * u);
+        }
+        u32x4 sreg[SPT], breg[SPT];
+        if (sb_vector) {
+            // unit v: row v / (CHUNK_G/8), groups 8*(v % (CHUNK_G/8)) .. +8 of the chunk
+#pragma unroll
+            for (int t = 0; t < SPT; ++t) {
+                const int v = min((int)threadIdx.x + t * kThreads, SBU - 1);
+                const int r = v / (CHUNK_G / 8);
+                const int gu = min(8 * (v % (CHUNK_G / 8)), ng - 8);
+                const size_t off = (size_t)min(wg_row0 + r, N - 1) * Kg + g0 + gu;
+                sreg[t] = *reinterpret_cast<const u32x4 *>(a.scales + off);
+                breg[t] = *reinterpret_cast<const u32x4 *>(a.biases + off);
+            }
+        }
+
+        // 2. Group of slot sl for this lane, relative to the chunk (lanes past
+        //    the chunk re-read its last group), and the weight prefetch ring.
+        //    Every weight load is unconditional, so the compiler can keep the
+        //    ring in flight; addresses are a wave-uniform row base plus a
+        //    32-bit lane offset.
+        int lgroup[SLOTS];
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl)
+            lgroup[sl] = min(lane + sl * kWave, ng - 1);
         auto load = [&](Stage &st, int task) {
             const int r = task / SLOTS, sl = task % SLOTS;
-            const int g = g0 + min(lane + sl * kWave, ng - 1);
-            load_words<NWG, ALIGN>(a.wq + rowoff[r] * wpr + (size_t)g * NWG, st.w);
-            const size_t sidx = rowoff[r] * Kg + g;
-            st.s = a.scales[sidx];
-            st.b = a.biases[sidx];
+            const uint32_t *wbase = a.wq + rowoff[r] * wpr + (size_t)g0 * NWG;
+            load_words<NWG, ALIGN>(byte_offset(wbase, (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
         };
-
 #pragma unroll
         for (int t = 0; t < PD; ++t)
             load(ring[t], t);
 
+        // 3. Stage the chunk in LDS: activations in the unpack's pair order
+        //    with their group sums, and one (scale, bias) pair per row and group.
         __syncthreads();  // all waves are done reading the previous chunk
-        for (int u = threadIdx.x; u < ng * UPG; u += kThreads) {
-            const half8_t v = *reinterpret_cast<const half8_t *>(a.x + (size_t)g0 * G + 8 * u);
-            xp[u] = to_pair_order8<BITS>(v);
-            float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int u = (int)threadIdx.x + t * kThreads;
+            const half8_t v = xreg[t];
+            float s8 = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s += (float)v[e];
+                s8 += (float)v[e];
 #pragma unroll
             for (int off = 1; off < UPG; off *= 2)
-                s += __shfl_xor(s, off);
-            if (u % UPG == 0)
-                xsum[u / UPG] = s;
+                s8 += __shfl_xor(s8, off);
+            if (u < ng * UPG) {
+                xp[u % UPG][u / UPG] = to_pair_order8<BITS>(v);
+                if (u % UPG == 0)
+                    xsum[u / UPG] = s8;
+            }
+        }
+        if (sb_vector) {
+#pragma unroll
+            for (int t = 0; t < SPT; ++t) {
+                const int v = (int)threadIdx.x + t * kThreads;
+                const int r = v / (CHUNK_G / 8);
+                const int gu = 8 * (v % (CHUNK_G / 8));
+                if (v < SBU && gu < ng) {
+                    const u32x4 sv = sreg[t], bv = breg[t];
+                    uint32_t *dst = &sbl[r][gu];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dst[2 * e] = __builtin_amdgcn_perm(bv[e], sv[e], 0x05040100u);      // (s_lo, b_lo)
+                        dst[2 * e + 1] = __builtin_amdgcn_perm(bv[e], sv[e], 0x07060302u);  // (s_hi, b_hi)
+                    }
+                }
+            }
+        } else {
+            for (int v = threadIdx.x; v < ROWS * ng; v += kThreads) {
+                const int r = v / ng, gl = v % ng;
+                const size_t off = (size_t)min(wg_row0 + r, N - 1) * Kg + g0 + gl;
+                sbl[r][gl] = (uint32_t)a.scales[off] | ((uint32_t)a.biases[off] << 16);
+            }
         }
         __syncthreads();
 
+        // 4. The (row, slot) tasks in program order, refilling the ring.
 #pragma unroll
         for (int t = 0; t < TASKS; ++t) {
+            // keep tasks in program order (no hoisting of later tasks' work,
+            // which would force early waits on their loads)
+            __builtin_amdgcn_sched_barrier(0);
             const int r = t / SLOTS, sl = t % SLOTS;
             Stage &st = ring[t % PD];
+#pragma unroll
+            for (int j = 0; j < NWG; ++j)
+                pin_register(st.w[j]);
             if (sl * kWave < ng) {
                 const int gl = lane + sl * kWave;
                 const int glc = min(gl, ng - 1);
@@ -132,13 +206,16 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                 float P = 0.f;
 #pragma unroll
                 for (int u = 0; u < UPG; ++u) {
-                    const half8_t xv = xp[glc * UPG + u];
+                    const half8_t xv = xp[u][glc];
                     P = __builtin_amdgcn_fdot2(q[4 * u + 0], half2_t{xv[0], xv[1]}, P, false);
                     P = __builtin_amdgcn_fdot2(q[4 * u + 1], half2_t{xv[2], xv[3]}, P, false);
                     P = __builtin_amdgcn_fdot2(q[4 * u + 2], half2_t{xv[4], xv[5]}, P, false);
                     P = __builtin_amdgcn_fdot2(q[4 * u + 3], half2_t{xv[6], xv[7]}, P, false);
                 }
-                const float contrib = half_bits_to_float(st.s) * P + half_bits_to_float(st.b) * xsum[glc];
+                const uint32_t sb = sbl[wave * RPW + r][glc];
+                const float sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
+                const float bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
+                const float contrib = sc * P + bias * xsum[glc];
                 acc[r] += gl < ng ? contrib : 0.f;
             }
             if (t + PD < TASKS)
@@ -154,13 +231,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     }
 }
 
-template <int BITS, int G, int SLOTS>
+template <int BITS, int G, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows>
 hipError_t launch_qmv_slots(const ProductArgs &a, hipStream_t stream)
 {
-    constexpr int RPW = kRowsPerWave;
     const int rows_per_block = kWaves * RPW;
     const dim3 grid((a.N + rows_per_block - 1) / rows_per_block, 1, a.split);
-    hipLaunchKernelGGL((qmv_kernel<BITS, G, SLOTS, RPW>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qmv_kernel<BITS, G, SLOTS, RPW, PD_ROWS>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
