@@ -49,6 +49,9 @@ EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_splitk", "qmm_splitk_workspa
             "qmm_validate", "qmm_strerror", "qmm_kernel_name", "qmm_forward_kernel")
 
 
+QMM_ERR_UNSUPPORTED = -9  # qmm_forward_kernel: the named kernel cannot run this shape
+
+
 class QmmError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: {qmm_strerror(code)} (code {code})")
@@ -144,7 +147,7 @@ def qmm_forward(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Ten
 
 def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,
                        out=None) -> torch.Tensor:
-    """qmm_forward with an explicitly named kernel ("qmv" or "mfma")."""
+    """qmm_forward with an explicitly named kernel ("qmv", "mfma" or "mfma_lds")."""
     M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)

@@ -30,33 +30,66 @@ int check_shape(int M, int K, int N, int bits, int G)
     return QMM_OK;
 }
 
-enum class Kernel { qmv, mfma };
+enum class Kernel { qmv, mfma, mfma_lds };
 
-Kernel choose_kernel(int M) { return M == 1 ? Kernel::qmv : Kernel::mfma; }
+const char *kernel_label(Kernel k)
+{
+    return k == Kernel::qmv ? "qmv" : k == Kernel::mfma ? "mfma" : "mfma_lds";
+}
 
-const char *kernel_label(Kernel k) { return k == Kernel::qmv ? "qmv" : "mfma"; }
+qmm::ProductArgs product_args(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                              const uint16_t *biases, float *y, int M, int K, int N, int split)
+{
+    qmm::ProductArgs a{};
+    a.x = x;
+    a.wq = wq;
+    a.scales = scales;
+    a.biases = biases;
+    a.y = y;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.split = split;
+    a.y_slice_stride = (size_t)M * N;
+    return a;
+}
 
-// Launch one product (all of M, in 16-row steps for the multi-row kernel)
+// The register-resident kernel's support depends on K, bits, G and the
+// split only; M and the pointers do not matter.
+bool xr_supported(int K, int N, int bits, int G, int split)
+{
+    const qmm::ProductArgs a = product_args(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                            kMaxRowsPerLaunch, K, N, split);
+    return qmm::mfma_xr_supported(a, bits, G);
+}
+
+Kernel choose_kernel(int M, int K, int N, int bits, int G, int split)
+{
+    if (M == 1)
+        return Kernel::qmv;
+    return xr_supported(K, N, bits, G, split) ? Kernel::mfma : Kernel::mfma_lds;
+}
+
+// Launch one product (all of M, in 16-row steps for the multi-row kernels)
 // writing either y (split == 1) or the split partials (y = workspace).
 int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
                    const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
                    int split, hipStream_t stream)
 {
-    qmm::ProductArgs a{};
-    a.wq = wq;
-    a.scales = scales;
-    a.biases = biases;
-    a.K = K;
-    a.N = N;
-    a.split = split;
-    a.y_slice_stride = (size_t)M * N;
+    if (kind == Kernel::mfma && !xr_supported(K, N, bits, G, split))
+        return QMM_ERR_UNSUPPORTED;
+    qmm::ProductArgs a = product_args(x, wq, scales, biases, y, M, K, N, split);
     const int step = kind == Kernel::qmv ? 1 : kMaxRowsPerLaunch;
     for (int m0 = 0; m0 < M; m0 += step) {
         a.M = M - m0 < step ? M - m0 : step;
         a.x = x + (size_t)m0 * K;
         a.y = y + (size_t)m0 * N;
-        const hipError_t e = kind == Kernel::qmv ? qmm::launch_qmv(a, bits, G, stream)
-                                                 : qmm::launch_mfma(a, bits, G, stream);
+        hipError_t e;
+        switch (kind) {
+        case Kernel::qmv: e = qmm::launch_qmv(a, bits, G, stream); break;
+        case Kernel::mfma: e = qmm::launch_mfma_xr(a, bits, G, stream); break;
+        default: e = qmm::launch_mfma(a, bits, G, stream); break;
+        }
         if (e != hipSuccess)
             return QMM_ERR_LAUNCH;
     }
@@ -79,6 +112,7 @@ const char *qmm_strerror(int code)
     case QMM_ERR_WORKSPACE: return "workspace smaller than qmm_splitk_workspace_bytes(M, N, split_k)";
     case QMM_ERR_ALIGN: return "x, wq, scales, biases, y and workspace must be 16-byte aligned";
     case QMM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case QMM_ERR_UNSUPPORTED: return "the requested kernel cannot run this shape";
     default: return "unknown error code";
     }
 }
@@ -115,7 +149,7 @@ const char *qmm_kernel_name(int M, int K, int N, int bits, int G)
 {
     if (check_shape(M, K, N, bits, G) != QMM_OK)
         return nullptr;
-    return kernel_label(choose_kernel(M));
+    return kernel_label(choose_kernel(M, K, N, bits, G, 1));
 }
 
 int qmm_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits, hipStream_t stream)
@@ -140,7 +174,8 @@ int qmm_forward(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
     const int rc = qmm_validate(x, wq, scales, biases, y, M, K, N, bits, G, 0, nullptr, 0);
     if (rc != QMM_OK)
         return rc;
-    return launch_product(choose_kernel(M), x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
+    return launch_product(choose_kernel(M, K, N, bits, G, 1), x, wq, scales, biases, y, M, K, N,
+                          bits, G, 1, stream);
 }
 
 int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
@@ -151,7 +186,7 @@ int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *sc
                                 split_k < 1 ? -1 : split_k, workspace, workspace_bytes);
     if (rc != QMM_OK)
         return rc;
-    const Kernel kind = choose_kernel(M);
+    const Kernel kind = choose_kernel(M, K, N, bits, G, split_k);
     if (split_k == 1)
         return launch_product(kind, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
     const int rc1 = launch_product(kind, x, wq, scales, biases, workspace, M, K, N, bits, G,
@@ -177,6 +212,8 @@ int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq
         kind = Kernel::qmv;
     else if (strcmp(kernel, "mfma") == 0)
         kind = Kernel::mfma;
+    else if (strcmp(kernel, "mfma_lds") == 0)
+        kind = Kernel::mfma_lds;
     else
         return QMM_ERR_SHAPE;
     return launch_product(kind, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);

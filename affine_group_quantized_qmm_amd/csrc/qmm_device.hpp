@@ -149,6 +149,17 @@ __device__ __forceinline__ half2_t code_pair4_offset64(uint32_t word)
     return __builtin_bit_cast(half2_t, and_or(v, mask, magic));
 }
 
+// The 8 activations of one MFMA K-block (8 consecutive codes of a lane's
+// chunk) rearranged into the pair order of unpack_pairs.
+template <int BITS>
+__device__ __forceinline__ half8_t to_pair_order(half8_t v)
+{
+    if constexpr (pair_dist(BITS) == 4)
+        return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
+    else
+        return __builtin_shufflevector(v, v, 0, 2, 1, 3, 4, 6, 5, 7);
+}
+
 // Offset every widened code carries (see code_pair4_offset64): the epilogue
 // uses s * (P' - kCodeOffset * XS) = s * P.
 template <int BITS>

@@ -30,6 +30,10 @@ hipError_t launch_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int
                        hipStream_t stream);
 hipError_t launch_qmv(const ProductArgs &a, int bits, int G, hipStream_t stream);
 hipError_t launch_mfma(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// Register-resident multi-row kernel: whether it can run `a` (split included)
+// and its launcher (hipErrorInvalidValue when it cannot).
+bool mfma_xr_supported(const ProductArgs &a, int bits, int G);
+hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size_t count,
                                 hipStream_t stream);
 

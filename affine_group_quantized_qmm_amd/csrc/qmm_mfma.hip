@@ -73,16 +73,6 @@ struct Geometry {
     }
 };
 
-// The 8 activations of one MFMA K-block in the unpack's pair order.
-template <int BITS>
-__device__ __forceinline__ half8_t to_pair_order(half8_t v)
-{
-    if constexpr (pair_dist(BITS) == 4)
-        return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
-    else
-        return __builtin_shufflevector(v, v, 0, 2, 1, 3, 4, 6, 5, 7);
-}
-
 // 4x4 transpose across the four 16-lane rows of a wave: on entry register t
 // of lane row c holds V[c][t]; on exit register t holds V[t][c].
 __device__ __forceinline__ void transpose4(uint32_t &w0, uint32_t &w1, uint32_t &w2, uint32_t &w3)

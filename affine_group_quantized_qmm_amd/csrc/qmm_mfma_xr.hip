@@ -1,0 +1,433 @@
+// Multi-row product (M = 2..16 activation rows) on the gfx950 matrix cores,
+// with each wave's share of the activations held in registers.
+//
+// The vmlx-swift pull request #565 page (commit "LaneQMM") contracts the raw
+// affine codes with a tensor-op matmul and applies the group scale and bias
+// after the dot product; this kernel does the same with
+// v_mfma_f32_16x16x32_f16 (lane = 16*c + i, c = 0..3):
+//   A (activations): lane (c, i) holds 8 values of activation row i,
+//   B (codes):       lane (c, i) holds 8 codes of weight row n0 + i,
+//   C (fp32):        lane (c, i) holds rows 4c..4c+3 of output column n0 + i.
+// Lane block c supplies codes c*G/4 .. c*G/4 + G/4 - 1 of a group, so G/32
+// accumulating MFMAs contract exactly one group into P_g, and the fp32
+// epilogue acc += s[n][g] * P_g applies that group's scale. The bias term
+// sum_g b[n][g] * XS[m][g] (XS: the activations' group sums) is itself a
+// small product over groups: one v_mfma_f32_16x16x4_f32 per quad of groups,
+// from group sums computed once per launch.
+//
+// Work split. A workgroup of KP waves walks a contiguous range of 16-row
+// tiles. Wave kp owns the kp-th of KP parts of the K range (at most 768
+// activations per row, 512 for 8-bit codes) and loads its A operands once,
+// into registers, for the whole launch; the KP partial tiles are summed
+// through LDS in a fixed order after every tile, so results do not depend
+// on timing.
+//
+// Weights. Every lane of a 16-byte load reads a consecutive piece of one
+// weight row, so one load instruction covers whole row segments (the 16 rows
+// x segment-bytes block of a tile and part), which is the access shape that
+// streams from HBM at full rate. The wave writes the block to its own LDS
+// region and reads back each lane's chunk in the MFMA B layout; the tile's
+// scales and biases go the same way, interleaved as (s | b << 16) words. The
+// loads of the next tile are issued as soon as the current one is in LDS, so
+// they stream while it is computed.
+#include "qmm_device.hpp"
+#include "qmm_kernels.hpp"
+
+namespace qmm {
+namespace {
+
+constexpr int kXrMaxParts = 8;    // waves (K parts) per workgroup
+
+// Activations per row held by one wave: 96 registers of A operands (64 for
+// 8-bit codes, whose tiles take more registers in flight).
+constexpr int xr_codes(int bits) { return bits == 8 ? 512 : 768; }
+
+template <int BITS, int G>
+struct XrGeo {
+    static constexpr int T = G / 32;                         // MFMAs per group
+    static constexpr int CH = G / 4;                         // codes per lane block per group
+    static constexpr int CHB = CH * BITS;                    // bits per lane block (multiple of 8)
+    static constexpr int GB = G * BITS / 8;                  // bytes per group (multiple of 4)
+    static constexpr int XG = xr_codes(BITS) / G;            // groups per part, at most
+    static constexpr int GRAN = 16 / gcd_int(GB, 16);        // part starts: multiples of GRAN groups
+    static constexpr int NI = (XG * GB + 63) / 64;           // 16-byte loads per lane per tile
+    static constexpr int LSTR = XG * GB + 16;                // LDS bytes per weight row
+    static constexpr int XQ = (XG + 3) / 4;                  // group quads per part
+    static constexpr int SBSTR = 4 * XQ + ((XQ % 2) ? 0 : 4); // LDS words per scale/bias row: 16-byte rows, odd quad count
+    static constexpr int max_shift()
+    {
+        int m = 0;
+        for (int c = 0; c < 4; ++c)
+            m = (c * CHB) % 32 > m ? (c * CHB) % 32 : m;
+        return m;
+    }
+    static constexpr int SHIFT = max_shift();
+    static constexpr int NWR = (SHIFT + CHB + 31) / 32;      // LDS words read per lane block
+    static constexpr int NWC = (CHB + 31) / 32;              // chunk words after the shift
+    static_assert(CHB % 8 == 0 && GB % 4 == 0, "chunks must start on byte boundaries");
+    static_assert(LSTR % 16 == 0, "weight rows must keep 16-byte LDS alignment");
+};
+
+struct XrArgs {
+    ProductArgs p;
+    int gran;    // part boundary granularity in groups
+    int ntiles;  // 16-row tiles of N
+};
+
+// Group range [pb, pe) of part kp: the slice [gb, ge) cut into KP parts of
+// whole granules of `gran` groups (the last granule may be short).
+__device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int gran, int &pb, int &pe)
+{
+    const int nu = (ge - gb + gran - 1) / gran;
+    int ub, ue;
+    slice_groups(nu, KP, kp, ub, ue);
+    pb = min(gb + ub * gran, ge);
+    pe = min(gb + ue * gran, ge);
+}
+
+// SBW: bytes per scale/bias load (4: two groups per load, 2: one group).
+template <int BITS, int G, int SBW>
+__global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
+{
+    using Geo = XrGeo<BITS, G>;
+    constexpr int T = Geo::T, CH = Geo::CH, GB = Geo::GB, XG = Geo::XG, NI = Geo::NI;
+    constexpr int LSTR = Geo::LSTR, SBSTR = Geo::SBSTR, NWR = Geo::NWR, NWC = Geo::NWC;
+    constexpr int SBE = SBW / 2;                             // groups per scale/bias load
+    constexpr int NS = (16 * XG / SBE + 63) / 64;            // scale (and bias) loads per lane per tile
+
+    __shared__ __align__(16) uint8_t wlds[kXrMaxParts][16 * LSTR];
+    __shared__ uint32_t sblds[kXrMaxParts][16 * SBSTR];
+    __shared__ float red[2][kXrMaxParts][4][kWave];
+
+    const ProductArgs &a = xa.p;
+    const int lane = threadIdx.x % kWave;
+    const int kp = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int KP = blockDim.x / kWave;
+    const int c = lane / 16, i = lane % 16;
+    const int M = a.M, K = a.K, N = a.N, Kg = K / G;
+    const uint32_t RB = (uint32_t)K * BITS / 8;  // bytes per weight row
+
+    int gb = 0, ge = Kg;
+    if (a.split > 1)
+        slice_groups(Kg, a.split, blockIdx.z, gb, ge);
+    int pb, pe;
+    part_range(gb, ge, KP, kp, xa.gran, pb, pe);
+    const int ng = pe - pb;  // >= 1 (the host never makes empty parts)
+
+    // tiles of this workgroup
+    const int t0 = (int)(((long long)blockIdx.x * xa.ntiles) / gridDim.x);
+    const int t1 = (int)(((long long)(blockIdx.x + 1) * xa.ntiles) / gridDim.x);
+
+    // Per-lane load geometry, fixed for the launch. Weight unit u (16 bytes)
+    // is row u / U, column u % U of the tile's 16 x (ng*GB) block.
+    const int U = ng * GB / 16;
+    int wr[NI];
+    uint32_t wcol[NI], wl[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int u = min(64 * j + lane, 16 * U - 1);
+        wr[j] = u / U;
+        wcol[j] = (uint32_t)pb * GB + (uint32_t)(u % U) * 16;
+        wl[j] = (uint32_t)wr[j] * LSTR + (uint32_t)(u % U) * 16;
+    }
+    const int V = ng / SBE;  // scale/bias units per row (ng is a multiple of SBE)
+    int sr[NS], scol[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int e = min(64 * j + lane, 16 * V - 1);
+        sr[j] = e / V;
+        scol[j] = e % V;
+    }
+
+    struct Stage {
+        u32x4 w[NI];
+        uint32_t s[NS], b[NS];
+    };
+    auto issue = [&](Stage &st, int tile) {
+        tile = min(tile, t1 - 1);
+        const int rmax = N - 1 - tile * 16;  // rows past N re-read row N-1
+        const uint8_t *wt = reinterpret_cast<const uint8_t *>(a.wq) + (size_t)tile * 16 * RB;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const uint32_t off = (uint32_t)min(wr[j], rmax) * RB + wcol[j];
+            st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(wt + off));
+        }
+        const size_t sbase = (size_t)tile * 16 * Kg + pb;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const uint32_t off = (uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE;
+            if constexpr (SBW == 4) {
+                st.s[j] = *reinterpret_cast<const uint32_t *>(a.scales + sbase + off);
+                st.b[j] = *reinterpret_cast<const uint32_t *>(a.biases + sbase + off);
+            } else {
+                st.s[j] = a.scales[sbase + off];
+                st.b[j] = a.biases[sbase + off];
+            }
+        }
+    };
+    uint8_t *const wmy = wlds[kp];
+    uint32_t *const sbmy = sblds[kp];
+    auto stage_to_lds = [&](Stage &st) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            *reinterpret_cast<u32x4 *>(wmy + wl[j]) = st.w[j];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            uint32_t *row = sbmy + sr[j] * SBSTR + scol[j] * SBE;
+            if constexpr (SBW == 4) {
+                row[0] = __builtin_amdgcn_perm(st.b[j], st.s[j], 0x05040100u);
+                row[1] = __builtin_amdgcn_perm(st.b[j], st.s[j], 0x07060302u);
+            } else {
+                row[0] = st.s[j] | (st.b[j] << 16);
+            }
+        }
+    };
+
+    Stage st;
+    issue(st, t0);
+
+    // A operands of this part, loaded once: lane (c, i) holds activation row
+    // min(i, M-1) (rows past M repeat the last row and are never stored).
+    half8_t xr[XG][T];
+    {
+        const uint16_t *xrow = a.x + (size_t)min(i, M - 1) * K;
+#pragma unroll
+        for (int g = 0; g < XG; ++g) {
+            const int gg = min(pb + g, pe - 1);  // groups past the part re-read its last group
+#pragma unroll
+            for (int h = 0; h < T; ++h)
+                xr[g][h] = to_pair_order<BITS>(
+                    *reinterpret_cast<const half8_t *>(xrow + (size_t)gg * G + c * CH + 8 * h));
+        }
+    }
+
+    // Group sums XS[row i][group 4u + c] of this part, as the A operand of
+    // one fp32 MFMA per group quad (the bias term sum_g b'[n][g] XS[m][g]).
+    // Lane block c holds a quarter of every group; the quarters meet in the
+    // (still unused) weight LDS region and are added in lane-block order.
+    float xsa[Geo::XQ];
+    {
+        float *xsl = reinterpret_cast<float *>(wmy);
+#pragma unroll
+        for (int g = 0; g < XG; ++g) {
+            float ps = 0.f;
+#pragma unroll
+            for (int h = 0; h < T; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ps += (float)xr[g][h][e];
+            xsl[(g * 4 + c) * 16 + i] = ps;
+        }
+#pragma unroll
+        for (int u = 0; u < Geo::XQ; ++u) {
+            const int g = 4 * u + c;
+            float v = 0.f;
+            if (g < ng) {
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+                    v += xsl[(g * 4 + cc) * 16 + i];
+            }
+            xsa[u] = v;
+        }
+        // scale/bias words of groups past the part stay zero: those groups
+        // (computed in whole quads) contribute nothing
+        for (int e = lane; e < 16 * SBSTR; e += kWave)
+            sbmy[e] = 0u;
+    }
+
+    const int chunk_byte = c * (Geo::CHB / 8);
+    const int chunk_shift = 8 * (chunk_byte % 4);
+    const uint8_t *wrow_lds = wmy + i * LSTR + (chunk_byte & ~3);
+    const uint32_t *sbrow = sbmy + i * SBSTR;
+    float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
+
+    auto process = [&](int tile, int par) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage_to_lds(st);
+        // the stage's registers are free again: start the next tile's loads
+        issue(st, tile + 1);
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < Geo::XQ; ++u) {
+            if (4 * u < ng) {  // wave-uniform
+                // the quad's MFMAs first, so their latency overlaps
+                float4_t P[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int g = 4 * u + t;
+                    P[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                    if (g < XG) {  // compile-time after unrolling
+                        uint32_t raw[NWR];
+#pragma unroll
+                        for (int w = 0; w < NWR; ++w)
+                            raw[w] = *reinterpret_cast<const uint32_t *>(wrow_lds + g * GB + 4 * w);
+                        uint32_t chunk[NWC];
+#pragma unroll
+                        for (int w = 0; w < NWC; ++w) {
+                            if constexpr (Geo::SHIFT == 0)
+                                chunk[w] = raw[w];
+                            else
+                                chunk[w] = w + 1 < NWR ? __builtin_amdgcn_alignbit(raw[w + 1], raw[w], chunk_shift)
+                                                       : (raw[w] >> chunk_shift);
+                        }
+                        half2_t q[CH / 2];
+                        unpack_pairs<BITS, CH>(chunk, q);
+#pragma unroll
+                        for (int h = 0; h < T; ++h) {
+                            const half8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
+                                               q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
+                            P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[g][h], B, P[t], 0, 0, 0);
+                        }
+                    }
+                }
+                // bias term of the quad: one fp32 MFMA over its 4 groups
+                const uint32_t sbo = sbrow[4 * u + c];
+                const float so = half_bits_to_float((uint16_t)(sbo & 0xffffu));
+                const float bo = half_bits_to_float((uint16_t)(sbo >> 16)) - CodeOffset<BITS>::value * so;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsa[u], bo, acc, 0, 0, 0);
+                // scale term: acc += s[n][g] * P_g
+                const u32x4 sbq = *reinterpret_cast<const u32x4 *>(sbrow + 4 * u);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (4 * u + t < XG) {
+                        const float sg = half_bits_to_float((uint16_t)(sbq[t] & 0xffffu));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[r] = __builtin_fmaf(sg, P[t][r], acc[r]);
+                    }
+                }
+            }
+        }
+        // fixed-order sum of the KP partial tiles
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            red[par][kp][r][lane] = acc[r];
+        __syncthreads();
+        if (kp == 0) {
+            const int col = tile * 16 + i;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = red[par][0][r][lane];
+                for (int p = 1; p < KP; ++p)
+                    v += red[par][p][r][lane];
+                const int m = 4 * c + r;
+                if (col < N && m < M)
+                    yout[(size_t)m * N + col] = v;
+            }
+        }
+    };
+
+    for (int t = t0; t < t1; t += 2) {
+        process(t, 0);
+        if (t + 1 < t1)  // uniform over the workgroup
+            process(t + 1, 1);
+    }
+}
+
+struct XrPlan {
+    int KP, gran, sbw;
+};
+
+// The register-resident kernel needs: whole 16-byte rows of packed codes,
+// K slices starting on a granule, at most kXrMaxParts parts of at most
+// xr_codes(BITS) activations each, and no empty part.
+template <int BITS, int G>
+bool plan_xr(const ProductArgs &a, XrPlan &plan)
+{
+    using Geo = XrGeo<BITS, G>;
+    const int Kg = a.K / G;
+    if (((long long)a.K * BITS) % 128 != 0)
+        return false;
+    const int sbw = Kg % 2 == 0 ? 4 : 2;
+    const int gran = sbw == 4 ? Geo::GRAN * 2 / gcd_int(Geo::GRAN, 2) : Geo::GRAN;
+    const int S = a.split;
+    int lmin = Kg, lmax = 0;
+    for (int z = 0; z < S; ++z) {
+        int b, e;
+        slice_groups(Kg, S, z, b, e);
+        if (b % gran != 0)
+            return false;
+        lmin = e - b < lmin ? e - b : lmin;
+        lmax = e - b > lmax ? e - b : lmax;
+    }
+    const int per_part = Geo::XG / gran;  // granules per part
+    if (per_part < 1)
+        return false;
+    const int nu_max = (lmax + gran - 1) / gran, nu_min = (lmin + gran - 1) / gran;
+    const int KP = (nu_max + per_part - 1) / per_part;
+    if (KP > kXrMaxParts || KP > nu_min)
+        return false;
+    // a part whose granule count is at its maximum must still fit
+    if (((nu_max + KP - 1) / KP) * gran > Geo::XG)
+        return false;
+    plan = XrPlan{KP, gran, sbw};
+    return true;
+}
+
+int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int BITS, int G>
+hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
+{
+    XrPlan plan;
+    done = plan_xr<BITS, G>(a, plan);
+    if (!done)
+        return hipSuccess;
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16};
+    // two waves per SIMD fit: 8 / KP workgroups per CU
+    const int per_cu = kXrMaxParts / plan.KP;
+    long long want = ((long long)device_cu_count() * per_cu + a.split - 1) / a.split;
+    const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
+    const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
+    if (plan.sbw == 4)
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 4>), grid, block, 0, stream, xa);
+    else
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 2>), grid, block, 0, stream, xa);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_xr_supported(const ProductArgs &a, int bits, int G)
+{
+    XrPlan plan;
+#define QMM_XR_CASE(B, GG) \
+    if (bits == B && G == GG) return plan_xr<B, GG>(a, plan);
+    QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)
+    QMM_XR_CASE(5, 32) QMM_XR_CASE(5, 64) QMM_XR_CASE(5, 128)
+    QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)
+    QMM_XR_CASE(8, 32) QMM_XR_CASE(8, 64) QMM_XR_CASE(8, 128)
+#undef QMM_XR_CASE
+    return false;
+}
+
+hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t stream)
+{
+    bool done = false;
+    hipError_t e = hipErrorInvalidValue;
+#define QMM_XR_CASE(B, GG) \
+    if (bits == B && G == GG) e = launch_xr_t<B, GG>(a, stream, done);
+    QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)
+    QMM_XR_CASE(5, 32) QMM_XR_CASE(5, 64) QMM_XR_CASE(5, 128)
+    QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)
+    QMM_XR_CASE(8, 32) QMM_XR_CASE(8, 64) QMM_XR_CASE(8, 128)
+#undef QMM_XR_CASE
+    if (e == hipSuccess && !done)
+        return hipErrorInvalidValue;
+    return e;
+}
+
+}  // namespace qmm

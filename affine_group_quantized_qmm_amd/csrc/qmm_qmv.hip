@@ -35,16 +35,6 @@ constexpr int kRowsPerWave = 4;
 constexpr int kPrefetchRows = 1;  // rows of loads kept in flight per wave
 constexpr int kMaxChunkK = 8192;  // activations staged per pass: at most 16 KB of fp16
 
-// The 8 activations of an aligned 8-code run in the unpack's pair order.
-template <int BITS>
-__device__ __forceinline__ half8_t to_pair_order8(half8_t v)
-{
-    if constexpr (pair_dist(BITS) == 4)
-        return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
-    else
-        return __builtin_shufflevector(v, v, 0, 2, 1, 3, 4, 6, 5, 7);
-}
-
 template <int BITS, int G, int SLOTS, int RPW, int PD_ROWS>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
@@ -157,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             for (int off = 1; off < UPG; off *= 2)
                 s8 += __shfl_xor(s8, off);
             if (u < ng * UPG) {
-                xp[u % UPG][u / UPG] = to_pair_order8<BITS>(v);
+                xp[u % UPG][u / UPG] = to_pair_order<BITS>(v);
                 if (u % UPG == 0)
                     xsum[u / UPG] = s8;
             }

@@ -68,6 +68,7 @@ extern "C" {
 #define QMM_ERR_WORKSPACE (-6)     /* workspace smaller than qmm_splitk_workspace_bytes */
 #define QMM_ERR_ALIGN (-7)         /* x, wq, scales, biases, y or workspace not 16-byte aligned */
 #define QMM_ERR_LAUNCH (-8)        /* the HIP runtime rejected a kernel launch */
+#define QMM_ERR_UNSUPPORTED (-9)   /* qmm_forward_kernel: that kernel cannot run this shape */
 
 /*
  * qmm_pack - pack unpacked codes into the bitstream layout above.
@@ -137,14 +138,24 @@ int qmm_validate(const void *x, const void *wq, const void *scales, const void *
 const char *qmm_strerror(int code);
 
 /* Name of the kernel qmm_forward would launch for these arguments
- * ("qmv" or "mfma") or NULL for invalid ones. Host-only. */
+ * ("qmv", "mfma" or "mfma_lds", see qmm_forward_kernel) or NULL for invalid
+ * ones. Host-only. */
 const char *qmm_kernel_name(int M, int K, int N, int bits, int G);
 
 /* qmm_forward with the kernel named explicitly instead of chosen from M
- * (a test and benchmark aid): "qmv" runs the one-row mat-vec once per
- * activation row (streaming the weights M times), "mfma" runs the multi-row
- * kernel. Same arguments, layout and errors as qmm_forward; an unknown name
- * returns QMM_ERR_SHAPE, a NULL name QMM_ERR_NULL. */
+ * (a test and benchmark aid):
+ *   "qmv"      the one-row mat-vec, once per activation row (streaming the
+ *              weights M times); qmm_forward's choice for M == 1;
+ *   "mfma"     the multi-row matrix-core kernel with each wave's K part of
+ *              the activations in registers; qmm_forward's choice for M >= 2
+ *              when the shape allows it (K * bits a multiple of 128 and K
+ *              short enough for 8 parts of 768 activations, 512 for 8-bit
+ *              codes); QMM_ERR_UNSUPPORTED otherwise;
+ *   "mfma_lds" the multi-row matrix-core kernel that streams activations
+ *              through LDS; any shape; qmm_forward's choice for M >= 2 when
+ *              "mfma" does not apply.
+ * Same arguments, layout and errors as qmm_forward; an unknown name returns
+ * QMM_ERR_SHAPE, a NULL name QMM_ERR_NULL. */
 int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,
                        const uint16_t *scales, const uint16_t *biases, float *y, int M,
                        int K, int N, int bits, int G, hipStream_t stream);

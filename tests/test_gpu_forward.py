@@ -26,14 +26,31 @@ def test_forward_small(bits, G, M):
     _gpu.assert_parity(y, ref, absum, f"forward bits={bits} G={G} M={M}")
 
 
-@pytest.mark.parametrize("kernel", ["qmv", "mfma"])
-@pytest.mark.parametrize("M", [1, 4, 16])
-@pytest.mark.parametrize("bits,G", [(4, 32), (5, 64), (6, 32), (8, 128)])
-def test_each_kernel(kernel, M, bits, G):
-    K, N = 40 * G, 97
-    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=11, M=M, K=K, N=N, bits=bits, G=G))
+KERNELS = ["qmv", "mfma", "mfma_lds"]
+
+
+def run_kernel(kernel, dp, bits, G):
+    """Forced-kernel call; "mfma" on a shape it cannot run must say so, and
+    then qmm_forward must not pick it."""
     qmm = _gpu.lib()
-    y = qmm.qmm_forward_kernel(kernel, dp.x, dp.wq, dp.s, dp.b, bits, G)
+    try:
+        return qmm.qmm_forward_kernel(kernel, dp.x, dp.wq, dp.s, dp.b, bits, G)
+    except qmm.QmmError as e:
+        assert kernel == "mfma" and e.code == qmm.QMM_ERR_UNSUPPORTED, str(e)
+        M, K, N = dp.p.M, dp.p.K, dp.p.N
+        assert qmm.qmm_kernel_name(max(M, 2), K, N, bits, G) == "mfma_lds"
+        return None
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("bits,G,K", [(4, 32, 1280), (5, 64, 2560), (6, 32, 1280), (8, 128, 2048),
+                                      (8, 64, 4096)])
+def test_each_kernel(kernel, M, bits, G, K):
+    N = 97
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=11, M=M, K=K, N=N, bits=bits, G=G))
+    y = run_kernel(kernel, dp, bits, G)
+    assert y is not None, f"{kernel} should support bits={bits} G={G} K={K}"
     torch.cuda.synchronize()
     ref, absum = dp.oracle()
     _gpu.assert_parity(y, ref, absum, f"{kernel} bits={bits} G={G} M={M}")
@@ -49,14 +66,18 @@ def test_more_than_16_rows(M):
     _gpu.assert_parity(y, ref, absum, f"M={M}")
 
 
-@pytest.mark.parametrize("kernel", ["qmv", "mfma"])
-@pytest.mark.parametrize("K,N", [(32, 1), (32, 64), (64, 5), (8192, 33), (8192 + 32, 17), (17408, 9)])
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("K,N", [(32, 1), (32, 64), (64, 5), (6144, 19), (6176, 23), (8192, 33),
+                                 (8192 + 32, 17), (17408, 9)])
 def test_edge_shapes(kernel, K, N):
-    """Single group, single row, one chunk exactly, one group past a chunk, long K."""
+    """Single group, single row, one chunk exactly, one group past a chunk, the
+    longest K the register-resident kernel takes and one group more, long K."""
     bits, G = 4, 32
     for M in (1, 5):
         dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=K + N + M, M=M, K=K, N=N, bits=bits, G=G))
-        y = _gpu.lib().qmm_forward_kernel(kernel, dp.x, dp.wq, dp.s, dp.b, bits, G)
+        y = run_kernel(kernel, dp, bits, G)
+        if y is None:
+            continue
         torch.cuda.synchronize()
         ref, absum = dp.oracle()
         _gpu.assert_parity(y, ref, absum, f"{kernel} K={K} N={N} M={M}")
@@ -71,7 +92,7 @@ def test_one_hot_columns(bits, G):
     p.M = K
     dp = _gpu.DeviceProblem(p)
     qmm = _gpu.lib()
-    for kernel in ("qmv", "mfma"):
+    for kernel in KERNELS:
         y = qmm.qmm_forward_kernel(kernel, dp.x, dp.wq, dp.s, dp.b, bits, G)
         torch.cuda.synchronize()
         ref, absum = dp.oracle()
