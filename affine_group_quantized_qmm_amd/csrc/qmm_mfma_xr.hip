@@ -18,9 +18,9 @@
 // Work split. A workgroup of KP waves walks a contiguous range of 16-row
 // tiles. Wave kp owns the kp-th of KP parts of the K range (at most 768
 // activations per row, 512 for 8-bit codes) and loads its A operands once,
-// into registers, for the whole launch; the KP partial tiles are summed
-// through LDS in a fixed order after every tile, so results do not depend
-// on timing.
+// into registers, for the whole launch. The KP partial tiles wait in LDS
+// and are summed in a fixed part order after every batch of tiles (one
+// barrier per batch), so results do not depend on timing.
 //
 // Weights. Every lane of a 16-byte load reads a consecutive piece of one
 // weight row, so one load instruction covers whole row segments (the 16 rows
@@ -28,8 +28,8 @@
 // streams from HBM at full rate. The wave writes the block to its own LDS
 // region and reads back each lane's chunk in the MFMA B layout; the tile's
 // scales and biases go the same way, interleaved as (s | b << 16) words. The
-// loads of the next tile are issued as soon as the current one is in LDS, so
-// they stream while it is computed.
+// loads of the tile NST ahead are issued as soon as the current one is in
+// LDS, so they stream while NST tiles are computed.
 #include "qmm_device.hpp"
 #include "qmm_kernels.hpp"
 
@@ -37,10 +37,14 @@ namespace qmm {
 namespace {
 
 constexpr int kXrMaxParts = 8;    // waves (K parts) per workgroup
+constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after one barrier
 
 // Activations per row held by one wave: 96 registers of A operands (64 for
 // 8-bit codes, whose tiles take more registers in flight).
 constexpr int xr_codes(int bits) { return bits == 8 ? 512 : 768; }
+
+// Tiles of loads in flight per wave: two where the registers allow it.
+constexpr int xr_stages(int bits) { return bits == 4 || bits == 8 ? 2 : 1; }
 
 template <int BITS, int G>
 struct XrGeo {
@@ -85,8 +89,23 @@ __device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int g
     pe = min(gb + ue * gran, ge);
 }
 
+// Dynamic LDS of one workgroup of KP waves: per wave a weight tile region
+// (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), then two
+// buffers of kXrBatch tiles of partial sums.
+template <int BITS, int G>
+__host__ __device__ constexpr size_t xr_wave_lds()
+{
+    return 16 * (size_t)XrGeo<BITS, G>::LSTR + 16 * 4 * (size_t)XrGeo<BITS, G>::SBSTR;
+}
+template <int BITS, int G>
+__host__ __device__ constexpr size_t xr_lds_bytes(int KP)
+{
+    return (size_t)KP * xr_wave_lds<BITS, G>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
+}
+
 // SBW: bytes per scale/bias load (4: two groups per load, 2: one group).
-template <int BITS, int G, int SBW>
+// NST: tiles of loads in flight per wave (register stages).
+template <int BITS, int G, int SBW, int NST>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
     using Geo = XrGeo<BITS, G>;
@@ -95,14 +114,19 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     constexpr int SBE = SBW / 2;                             // groups per scale/bias load
     constexpr int NS = (16 * XG / SBE + 63) / 64;            // scale (and bias) loads per lane per tile
 
-    __shared__ __align__(16) uint8_t wlds[kXrMaxParts][16 * LSTR];
-    __shared__ uint32_t sblds[kXrMaxParts][16 * SBSTR];
-    __shared__ float red[2][kXrMaxParts][4][kWave];
+    extern __shared__ __align__(16) uint8_t xr_lds[];
 
     const ProductArgs &a = xa.p;
     const int lane = threadIdx.x % kWave;
     const int kp = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int KP = blockDim.x / kWave;
+    uint8_t *const wmy = xr_lds + (size_t)kp * xr_wave_lds<BITS, G>();
+    uint32_t *const sbmy = reinterpret_cast<uint32_t *>(wmy + 16 * LSTR);
+    // red[buf][slot][part][r][lane]
+    float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G>());
+    auto red_at = [&](int buf, int slot, int part, int r) -> float & {
+        return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
+    };
     const int c = lane / 16, i = lane % 16;
     const int M = a.M, K = a.K, N = a.N, Kg = K / G;
     const uint32_t RB = (uint32_t)K * BITS / 8;  // bytes per weight row
@@ -143,19 +167,26 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         u32x4 w[NI];
         uint32_t s[NS], b[NS];
     };
+    // Loads of one tile. Past the workgroup's last tile every lane reads the
+    // first 16 bytes of that tile instead (one cache line, never used), so
+    // the loads stay unconditional without streaming a tile twice.
     auto issue = [&](Stage &st, int tile) {
+        // a per-lane mask instead of a branch on `past`: a branch around
+        // loads makes the compiler drain every load in flight
+        uint32_t keep = tile >= t1 ? 0u : ~0u;
+        pin_register(keep);
         tile = min(tile, t1 - 1);
         const int rmax = N - 1 - tile * 16;  // rows past N re-read row N-1
         const uint8_t *wt = reinterpret_cast<const uint8_t *>(a.wq) + (size_t)tile * 16 * RB;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const uint32_t off = (uint32_t)min(wr[j], rmax) * RB + wcol[j];
+            const uint32_t off = ((uint32_t)min(wr[j], rmax) * RB + wcol[j]) & keep;
             st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(wt + off));
         }
         const size_t sbase = (size_t)tile * 16 * Kg + pb;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const uint32_t off = (uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE;
+            const uint32_t off = ((uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE) & keep;
             if constexpr (SBW == 4) {
                 st.s[j] = *reinterpret_cast<const uint32_t *>(a.scales + sbase + off);
                 st.b[j] = *reinterpret_cast<const uint32_t *>(a.biases + sbase + off);
@@ -165,8 +196,6 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
             }
         }
     };
-    uint8_t *const wmy = wlds[kp];
-    uint32_t *const sbmy = sblds[kp];
     auto stage_to_lds = [&](Stage &st) {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
@@ -183,9 +212,6 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         }
     };
 
-    Stage st;
-    issue(st, t0);
-
     // A operands of this part, loaded once: lane (c, i) holds activation row
     // min(i, M-1) (rows past M repeat the last row and are never stored).
     half8_t xr[XG][T];
@@ -200,6 +226,13 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     *reinterpret_cast<const half8_t *>(xrow + (size_t)gg * G + c * CH + 8 * h));
         }
     }
+
+    // The first NST tiles' loads, issued after the activation loads so that
+    // the loop always finds its stages in the same order of age.
+    Stage st[NST];
+#pragma unroll
+    for (int k = 0; k < NST; ++k)
+        issue(st[k], t0 + k);
 
     // Group sums XS[row i][group 4u + c] of this part, as the A operand of
     // one fp32 MFMA per group quad (the bias term sum_g b'[n][g] XS[m][g]).
@@ -241,11 +274,11 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     const uint32_t *sbrow = sbmy + i * SBSTR;
     float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
 
-    auto process = [&](int tile, int par) {
+    auto process = [&](Stage &sk, int tile) {
         __builtin_amdgcn_sched_barrier(0);
-        stage_to_lds(st);
-        // the stage's registers are free again: start the next tile's loads
-        issue(st, tile + 1);
+        stage_to_lds(sk);
+        // the stage's registers are free again: start the loads NST tiles ahead
+        issue(sk, tile + NST);
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < Geo::XQ; ++u) {
@@ -298,30 +331,41 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 }
             }
         }
-        // fixed-order sum of the KP partial tiles
+        // Partial sums wait in LDS; after every kXrBatch tiles (and the last)
+        // one barrier, then wave p sums slot p's KP partials in part order.
+        const int lt = tile - t0;
+        const int buf = (lt / kXrBatch) & 1, slot = lt % kXrBatch;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            red[par][kp][r][lane] = acc[r];
-        __syncthreads();
-        if (kp == 0) {
-            const int col = tile * 16 + i;
+            red_at(buf, slot, kp, r) = acc[r];
+        if (slot == kXrBatch - 1 || tile == t1 - 1) {  // uniform over the workgroup
+            __syncthreads();
+            const int first = tile - slot;
+            for (int sl = kp; sl <= slot; sl += KP) {
+                const int col = (first + sl) * 16 + i;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = red[par][0][r][lane];
-                for (int p = 1; p < KP; ++p)
-                    v += red[par][p][r][lane];
-                const int m = 4 * c + r;
-                if (col < N && m < M)
-                    yout[(size_t)m * N + col] = v;
+                for (int r = 0; r < 4; ++r) {
+                    float v = red_at(buf, sl, 0, r);
+                    for (int p = 1; p < KP; ++p)
+                        v += red_at(buf, sl, p, r);
+                    const int m = 4 * c + r;
+                    if (col < N && m < M)
+                        yout[(size_t)m * N + col] = v;
+                }
             }
         }
     };
 
-    for (int t = t0; t < t1; t += 2) {
-        process(t, 0);
-        if (t + 1 < t1)  // uniform over the workgroup
-            process(t + 1, 1);
+    // Whole rounds of NST tiles, then the remainder: no path around a stage's
+    // loads reaches the loop's back edge, so the waits stay per stage.
+    int t = t0;
+    for (; t + NST <= t1; t += NST) {
+#pragma unroll
+        for (int k = 0; k < NST; ++k)
+            process(st[k], t + k);
     }
+    if (t < t1)  // uniform over the workgroup; at most NST - 1 tiles left
+        process(st[0], t);
 }
 
 struct XrPlan {
@@ -392,10 +436,25 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
     long long want = ((long long)device_cu_count() * per_cu + a.split - 1) / a.split;
     const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
     const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
+    const size_t lds = xr_lds_bytes<BITS, G>(plan.KP);
+    constexpr int NST = xr_stages(BITS);
+    // more than 64 KB of dynamic LDS must be allowed per kernel, once
+    static bool allowed = false;
+    if (!allowed) {
+        const int cap = (int)xr_lds_bytes<BITS, G>(kXrMaxParts);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, 4, NST>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, 2, NST>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+        if (e != hipSuccess)
+            return e;
+        allowed = true;
+    }
     if (plan.sbw == 4)
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 4>), grid, block, 0, stream, xa);
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 4, NST>), grid, block, lds, stream, xa);
     else
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 2>), grid, block, 0, stream, xa);
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 2, NST>), grid, block, lds, stream, xa);
     return hipGetLastError();
 }
 
