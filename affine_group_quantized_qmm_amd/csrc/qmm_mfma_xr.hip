@@ -236,19 +236,21 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
 
     // Group sums XS[row i][group 4u + c] of this part, as the A operand of
     // one fp32 MFMA per group quad (the bias term sum_g b'[n][g] XS[m][g]).
-    // Lane block c holds a quarter of every group; the quarters meet in the
-    // (still unused) weight LDS region and are added in lane-block order.
+    // Lane block c sums its quarter of every group with v_dot2 against
+    // (1, 1); the quarters meet in the (still unused) weight LDS region and
+    // are added in lane-block order.
     float xsa[Geo::XQ];
     {
         float *xsl = reinterpret_cast<float *>(wmy);
+        const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int g = 0; g < XG; ++g) {
             float ps = 0.f;
 #pragma unroll
             for (int h = 0; h < T; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ps += (float)xr[g][h][e];
+                for (int e = 0; e < 8; e += 2)
+                    ps = __builtin_amdgcn_fdot2(half2_t{xr[g][h][e], xr[g][h][e + 1]}, one2, ps, false);
             xsl[(g * 4 + c) * 16 + i] = ps;
         }
 #pragma unroll
