@@ -11,10 +11,24 @@ value = weight bytes streamed per step / step time, where weight bytes per
 call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 
 Prints one JSON line. Synthetic data (seeded; no trained weights).
+
+The roofline object covers the kernel that takes most of a step. Its
+`traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE and
+WRITE_SIZE summary committed under profiles/, scaled by the counts the same
+counters give for a plain elementwise copy of known size, and is reported
+only while the kernel's sources still match the fingerprint recorded with
+the counters. Helper modes (used with rocprofv3, see profiles/):
+  --profile-run             a few launches of every cell plus the copy
+                            calibration, no timing;
+  --summarize-pmc F W OUT   counters CSV directories (FETCH_SIZE run, then
+                            WRITE_SIZE run) -> text summary OUT;
+  --summarize-trace D OUT   kernel-trace stats directory -> text summary OUT.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +47,17 @@ from qmm_inputs import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 ROTATION_BYTES = 512 * 2 ** 20
 CELLS_M = (1, 4, 16)
+CSRC = ROOT / "affine_group_quantized_qmm_amd" / "csrc"
+# sources that determine each kernel's memory traffic
+KERNEL_SOURCES = {
+    "mfma": ["qmm_mfma_xr.hip", "qmm_device.hpp", "qmm_kernels.hpp"],
+    "mfma_lds": ["qmm_mfma.hip", "qmm_device.hpp", "qmm_kernels.hpp"],
+    "qmv": ["qmm_qmv.hip", "qmm_device.hpp", "qmm_kernels.hpp"],
+}
+# rocprofv3 kernel-name fragments of the library's kernels
+KERNEL_SYMBOLS = {"mfma": "mfma_xr_kernel", "mfma_lds": "mfma_kernel<", "qmv": "qmv_kernel"}
+PMC_SUMMARY = ROOT / "profiles" / "dense_up_w4g32_hbm_traffic.txt"
+COPY_ELEMS = 64 * 2 ** 20  # fp32 elements of the calibration copy (256 MiB read, 256 MiB written)
 
 
 def parse():
@@ -43,7 +68,134 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="output rows of the CPU oracle sample (0: all rows)")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
     return ap.parse_args()
+
+
+def fingerprint(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        h.update((CSRC / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(directory: str):
+    """(dispatch index, kernel name, counter, value) from a rocprofv3 counter CSV."""
+    files = sorted(Path(directory).rglob("*counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                             float(r["Counter_Value"])))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """Counter value per dispatch (summed over instances), in dispatch order."""
+    acc = {}
+    for d, name, c, v in rows:
+        if c == counter:
+            k = acc.setdefault(d, [name, 0.0])
+            k[1] += v
+    return [(d, acc[d][0], acc[d][1]) for d in sorted(acc)]
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the profile run -> text summary."""
+    fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
+    # the profile run launches, in order: PROFILE_REPS rounds of the three cells, then
+    # PROFILE_REPS calibration copies
+    def classify(seq):
+        ours = [(n, v) for _, n, v in seq if "qmm::" in n]
+        other = [(n, v) for _, n, v in seq if "qmm::" not in n]
+        return ours, other
+    f_ours, f_copy = classify(fetch)
+    w_ours, w_copy = classify(write)
+    # the calibration copies are the last PROFILE_REPS non-library dispatches (earlier
+    # ones are the uploads of the inputs); the first of them runs on cold caches
+    f_copy, w_copy = f_copy[-PROFILE_REPS + 1:], w_copy[-PROFILE_REPS + 1:]
+    copy_bytes = 4 * COPY_ELEMS
+    f_copy_kib = sum(v for _, v in f_copy) / len(f_copy)
+    w_copy_kib = sum(v for _, v in w_copy) / len(w_copy)
+    f_scale = copy_bytes / (f_copy_kib * 1024)
+    w_scale = copy_bytes / (w_copy_kib * 1024)
+    cells = {}
+    for idx, ((fn, fv), (wn, wv)) in enumerate(zip(f_ours, w_ours)):
+        M = CELLS_M[idx % len(CELLS_M)]
+        kind = next(k for k, sym in KERNEL_SYMBOLS.items() if sym in fn)
+        if idx < len(CELLS_M):  # first round: cold caches, not used
+            continue
+        c = cells.setdefault(M, {"kernel": kind, "fetch": [], "write": []})
+        c["fetch"].append(fv)
+        c["write"].append(wv)
+    lines = [
+        "# HBM traffic of the dense-up W4 g32 cells (K=5120, N=17408), rocprofv3 counters",
+        "# commands (from the repository root on the GPU host):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o run -- python3 bench.py --profile-run",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o run -- python3 bench.py --profile-run",
+        f"#   python3 bench.py --summarize-pmc <F> <W> {Path(out).relative_to(ROOT) if Path(out).is_absolute() else out}",
+        f"copy_calibration kernel={f_copy[0][0].split('(')[0][:60].replace(' ', '_')} "
+        f"bytes={copy_bytes} fetch_kib={f_copy_kib:.1f} write_kib={w_copy_kib:.1f} "
+        f"fetch_scale={f_scale:.4f} write_scale={w_scale:.4f}",
+    ]
+    for M, c in sorted(cells.items()):
+        fk = sum(c["fetch"]) / len(c["fetch"])
+        wk = sum(c["write"]) / len(c["write"])
+        hbm = fk * 1024 * f_scale + wk * 1024 * w_scale
+        lines.append(f"cell M={M} kernel={c['kernel']} fingerprint={fingerprint(c['kernel'])} "
+                     f"fetch_kib={fk:.1f} write_kib={wk:.1f} hbm_bytes={hbm:.0f} dispatches={len(c['fetch'])}")
+    Path(out).write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic(kernel: str, Ms):
+    """Average HBM bytes per launch of `kernel` over cells Ms, or None (no summary, or
+    the kernel changed since the counters were taken)."""
+    if not PMC_SUMMARY.exists():
+        return None
+    got = {}
+    for line in PMC_SUMMARY.read_text().splitlines():
+        if not line.startswith("cell "):
+            continue
+        kv = dict(t.split("=", 1) for t in line.split()[1:])
+        if kv["kernel"] == kernel and kv["fingerprint"] == fingerprint(kernel):
+            got[int(kv["M"])] = float(kv["hbm_bytes"])
+    if any(M not in got for M in Ms):
+        return None
+    return sum(got[M] for M in Ms) / len(Ms)
+
+
+def summarize_trace(trace_dir: str, out: str):
+    """Kernel-trace stats of a bench run -> text summary (library kernels first)."""
+    files = sorted(Path(trace_dir).rglob("*kernel_stats.csv"))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0], newline="")))
+    lines = [
+        "# rocprofv3 kernel-trace stats of a bench run (dense-up W4 g32, M = 1, 4, 16)",
+        "# commands (from the repository root on the GPU host):",
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d <D> -o run -- "
+        "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+        f"#   python3 bench.py --summarize-trace <D> {out}",
+        "# name | calls | average_us | min_us | max_us | total_percent",
+    ]
+    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    for r in rows:
+        name = r["Name"]
+        short = next((k for k, sym in KERNEL_SYMBOLS.items() if sym in name), None)
+        label = f"{short}: {name}" if short else name
+        lines.append(f"{label[:140]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                     f"{float(r['Percentage']):.2f}")
+    Path(out).write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def make_copies(shape, dev, seed=0):
@@ -71,7 +223,7 @@ def time_launches(fn, reps: int, stream) -> float:
     return start.elapsed_time(stop) / reps
 
 
-def cpu_baseline(p, shape, rows: int):
+def cpu_baseline(p, shape, rows: int, min_seconds: float = 10.0):
     """The fp64 oracle on the host cores, on a bounded sample of output rows."""
     import oracle
     o = oracle.get()
@@ -79,24 +231,40 @@ def cpu_baseline(p, shape, rows: int):
     rng = np.random.default_rng(1)
     rows = shape.N if rows <= 0 else min(rows, shape.N)
     sel = np.sort(rng.choice(shape.N, size=rows, replace=False))
+    # whole passes (one call at each M over the sampled rows) until about 10 s of work
+    passes = 0
     t0 = time.perf_counter()
-    for M in CELLS_M:
-        o.forward_rows(p.x[:M], p.words, p.scales, p.biases, shape.bits, shape.G, sel,
-                       nthreads=threads)
-    dt = time.perf_counter() - t0
-    sample_bytes = len(CELLS_M) * sel.size * (shape.weight_bytes / shape.N)
+    while True:
+        for M in CELLS_M:
+            o.forward_rows(p.x[:M], p.words, p.scales, p.biases, shape.bits, shape.G, sel,
+                           nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 1000:
+            break
+    sample_bytes = passes * len(CELLS_M) * sel.size * (shape.weight_bytes / shape.N)
     return {
         "value": round(sample_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{sel.size} of {shape.N} output rows of {shape.name}, one pass at each of "
-                   f"M={list(CELLS_M)}; fp64 dequantize-then-dot; {dt:.2f} s"),
+        "sample": (f"{passes} passes over {sel.size} of {shape.N} output rows of {shape.name}, "
+                   f"each pass one call at each of M={list(CELLS_M)}; fp64 dequantize-then-dot; "
+                   f"{dt:.1f} s"),
     }
+
+
+PROFILE_REPS = 4
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the product shards along N "
               "with no exchange, so there is no multi-GPU measurement to make here", file=sys.stderr)
@@ -121,6 +289,17 @@ def main():
         for M in CELLS_M:
             call(M, counter[0])
             counter[0] += 1
+
+    if args.profile_run:
+        for _ in range(PROFILE_REPS):
+            step()
+        src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(PROFILE_REPS):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"profile run: {PROFILE_REPS} rounds of M={list(CELLS_M)}, {PROFILE_REPS} copies", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -151,9 +330,16 @@ def main():
             "algorithmic_bytes": algo,
             "rows_outputs_per_s": round(M * shape.N / (ms * 1e-3), 1),
         }
-    dominant = max(cells, key=lambda k: cells[k]["us_per_call"])
-    dom = cells[dominant]
-    achieved = dom["algorithmic_bytes"] / (dom["us_per_call"] * 1e-6) / 1e9
+    # the kernel with the largest share of a step, over all of its launches
+    by_kernel = {}
+    for key, c in cells.items():
+        by_kernel.setdefault(c["kernel"], []).append(int(key[1:]))
+    dominant = max(by_kernel, key=lambda k: sum(cells[f"M{M}"]["us_per_call"] for M in by_kernel[k]))
+    dom_Ms = by_kernel[dominant]
+    dom_us = sum(cells[f"M{M}"]["us_per_call"] for M in dom_Ms) / len(dom_Ms)
+    dom_bytes = sum(cells[f"M{M}"]["algorithmic_bytes"] for M in dom_Ms) / len(dom_Ms)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = read_traffic(dominant, dom_Ms)
 
     weight_bytes_per_step = len(CELLS_M) * shape.weight_bytes
     value = weight_bytes_per_step / (ms_per_step * 1e-3) / 1e9
@@ -180,13 +366,15 @@ def main():
         "cells": cells,
         "m16_over_m1_time": round(cells["M16"]["us_per_call"] / cells["M1"]["us_per_call"], 3),
         "roofline": {
-            "kernel": f"{dom['kernel']} (M={dominant[1:]})",
+            "kernel": f"{dominant} (M={','.join(str(M) for M in dom_Ms)}; per-launch averages)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "algorithmic_bytes_per_launch": round(dom_bytes),
+            "us_per_launch": round(dom_us, 3),
+            "traffic": None if traffic is None else round(traffic),
         },
     }
     if not args.no_cpu_baseline:
