@@ -39,20 +39,28 @@ namespace {
 constexpr int kXrMaxParts = 8;    // waves (K parts) per workgroup
 constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after one barrier
 
-// Activations per row held by one wave: 96 registers of A operands (64 for
-// 8-bit codes, whose tiles take more registers in flight).
-constexpr int xr_codes(int bits) { return bits == 8 ? 512 : 768; }
+// Activations per row held by one wave (XC: 640 or 768, 512 for 8-bit codes,
+// i.e. 80 to 96 registers of A operands) and tiles of loads in flight per
+// wave (register stages), as the registers allow. The host takes the first
+// variant of a width whose parts fit the workgroup (xr_variants).
+constexpr int xr_stages(int bits, int xc)
+{
+    return bits == 4 ? (xc <= 640 ? 3 : 2) : bits == 8 ? 2 : (xc <= 640 ? 2 : 1);
+}
+// Two-byte scale/bias loads (odd group counts) take twice the load registers:
+// one stage fewer, so that no variant spills.
+constexpr int xr_stages_sbw(int bits, int xc, int sbw)
+{
+    return sbw == 4 || xr_stages(bits, xc) == 1 ? xr_stages(bits, xc) : xr_stages(bits, xc) - 1;
+}
 
-// Tiles of loads in flight per wave: two where the registers allow it.
-constexpr int xr_stages(int bits) { return bits == 4 || bits == 8 ? 2 : 1; }
-
-template <int BITS, int G>
+template <int BITS, int G, int XC>
 struct XrGeo {
     static constexpr int T = G / 32;                         // MFMAs per group
     static constexpr int CH = G / 4;                         // codes per lane block per group
     static constexpr int CHB = CH * BITS;                    // bits per lane block (multiple of 8)
     static constexpr int GB = G * BITS / 8;                  // bytes per group (multiple of 4)
-    static constexpr int XG = xr_codes(BITS) / G;            // groups per part, at most
+    static constexpr int XG = XC / G;                        // groups per part, at most
     static constexpr int GRAN = 16 / gcd_int(GB, 16);        // part starts: multiples of GRAN groups
     static constexpr int NI = (XG * GB + 63) / 64;           // 16-byte loads per lane per tile
     static constexpr int LSTR = XG * GB + 16;                // LDS bytes per weight row
@@ -92,23 +100,23 @@ __device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int g
 // Dynamic LDS of one workgroup of KP waves: per wave a weight tile region
 // (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), then two
 // buffers of kXrBatch tiles of partial sums.
-template <int BITS, int G>
+template <int BITS, int G, int XC>
 __host__ __device__ constexpr size_t xr_wave_lds()
 {
-    return 16 * (size_t)XrGeo<BITS, G>::LSTR + 16 * 4 * (size_t)XrGeo<BITS, G>::SBSTR;
+    return 16 * (size_t)XrGeo<BITS, G, XC>::LSTR + 16 * 4 * (size_t)XrGeo<BITS, G, XC>::SBSTR;
 }
-template <int BITS, int G>
+template <int BITS, int G, int XC>
 __host__ __device__ constexpr size_t xr_lds_bytes(int KP)
 {
-    return (size_t)KP * xr_wave_lds<BITS, G>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
+    return (size_t)KP * xr_wave_lds<BITS, G, XC>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
 }
 
 // SBW: bytes per scale/bias load (4: two groups per load, 2: one group).
 // NST: tiles of loads in flight per wave (register stages).
-template <int BITS, int G, int SBW, int NST>
+template <int BITS, int G, int XC, int SBW, int NST>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
-    using Geo = XrGeo<BITS, G>;
+    using Geo = XrGeo<BITS, G, XC>;
     constexpr int T = Geo::T, CH = Geo::CH, GB = Geo::GB, XG = Geo::XG, NI = Geo::NI;
     constexpr int LSTR = Geo::LSTR, SBSTR = Geo::SBSTR, NWR = Geo::NWR, NWC = Geo::NWC;
     constexpr int SBE = SBW / 2;                             // groups per scale/bias load
@@ -120,10 +128,10 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     const int lane = threadIdx.x % kWave;
     const int kp = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int KP = blockDim.x / kWave;
-    uint8_t *const wmy = xr_lds + (size_t)kp * xr_wave_lds<BITS, G>();
+    uint8_t *const wmy = xr_lds + (size_t)kp * xr_wave_lds<BITS, G, XC>();
     uint32_t *const sbmy = reinterpret_cast<uint32_t *>(wmy + 16 * LSTR);
     // red[buf][slot][part][r][lane]
-    float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G>());
+    float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G, XC>());
     auto red_at = [&](int buf, int slot, int part, int r) -> float & {
         return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
     };
@@ -281,6 +289,8 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         stage_to_lds(sk);
         // the stage's registers are free again: start the loads NST tiles ahead
         issue(sk, tile + NST);
+        if (tile >= t1)  // uniform over the workgroup: a round's tail past the range
+            return;
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < Geo::XQ; ++u) {
@@ -358,16 +368,15 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         }
     };
 
-    // Whole rounds of NST tiles, then the remainder: no path around a stage's
-    // loads reaches the loop's back edge, so the waits stay per stage.
-    int t = t0;
-    for (; t + NST <= t1; t += NST) {
+    // Rounds of NST tiles, one per stage. Every round stages and reloads all
+    // NST stages (tiles past the range load one cache line and are not
+    // computed), so no path around a stage's loads reaches the back edge and
+    // the waits stay per stage.
+    for (int t = t0; t < t1; t += NST) {
 #pragma unroll
         for (int k = 0; k < NST; ++k)
             process(st[k], t + k);
     }
-    if (t < t1)  // uniform over the workgroup; at most NST - 1 tiles left
-        process(st[0], t);
 }
 
 struct XrPlan {
@@ -376,11 +385,11 @@ struct XrPlan {
 
 // The register-resident kernel needs: whole 16-byte rows of packed codes,
 // K slices starting on a granule, at most kXrMaxParts parts of at most
-// xr_codes(BITS) activations each, and no empty part.
-template <int BITS, int G>
+// XC activations each, and no empty part.
+template <int BITS, int G, int XC>
 bool plan_xr(const ProductArgs &a, XrPlan &plan)
 {
-    using Geo = XrGeo<BITS, G>;
+    using Geo = XrGeo<BITS, G, XC>;
     const int Kg = a.K / G;
     if (((long long)a.K * BITS) % 128 != 0)
         return false;
@@ -425,39 +434,71 @@ int device_cu_count()
     return cached[dev];
 }
 
-template <int BITS, int G>
-hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
+template <int BITS, int G, int XC>
+hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
-    XrPlan plan;
-    done = plan_xr<BITS, G>(a, plan);
-    if (!done)
-        return hipSuccess;
     XrArgs xa{a, plan.gran, (a.N + 15) / 16};
     // two waves per SIMD fit: 8 / KP workgroups per CU
     const int per_cu = kXrMaxParts / plan.KP;
     long long want = ((long long)device_cu_count() * per_cu + a.split - 1) / a.split;
     const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
     const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
-    const size_t lds = xr_lds_bytes<BITS, G>(plan.KP);
-    constexpr int NST = xr_stages(BITS);
+    const size_t lds = xr_lds_bytes<BITS, G, XC>(plan.KP);
+    constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
     // more than 64 KB of dynamic LDS must be allowed per kernel, once
     static bool allowed = false;
     if (!allowed) {
-        const int cap = (int)xr_lds_bytes<BITS, G>(kXrMaxParts);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, 4, NST>),
+        const int cap = (int)xr_lds_bytes<BITS, G, XC>(kXrMaxParts);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, cap);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, 2, NST>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, cap);
         if (e != hipSuccess)
             return e;
         allowed = true;
     }
     if (plan.sbw == 4)
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 4, NST>), grid, block, lds, stream, xa);
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4>), grid, block, lds, stream, xa);
     else
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, 2, NST>), grid, block, lds, stream, xa);
+        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2>), grid, block, lds, stream, xa);
     return hipGetLastError();
+}
+
+// Variants of a width, preferred first: fewer activation registers leave
+// room for more tiles in flight; the longer parts take longer K.
+template <int BITS>
+constexpr int xr_small_codes() { return BITS == 8 ? 512 : 640; }
+template <int BITS>
+constexpr int xr_large_codes() { return BITS == 8 ? 512 : 768; }
+
+template <int BITS, int G>
+bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
+{
+    if (plan_xr<BITS, G, xr_small_codes<BITS>()>(a, plan)) {
+        xc = xr_small_codes<BITS>();
+        return true;
+    }
+    if (plan_xr<BITS, G, xr_large_codes<BITS>()>(a, plan)) {
+        xc = xr_large_codes<BITS>();
+        return true;
+    }
+    return false;
+}
+
+template <int BITS, int G>
+hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
+{
+    XrPlan plan;
+    int xc = 0;
+    done = plan_xr_any<BITS, G>(a, plan, xc);
+    if (!done)
+        return hipSuccess;
+    if (xc == xr_small_codes<BITS>())
+        return launch_xr_variant<BITS, G, xr_small_codes<BITS>()>(a, plan, stream);
+    if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>())
+        return launch_xr_variant<BITS, G, xr_large_codes<BITS>()>(a, plan, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -465,8 +506,9 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
 bool mfma_xr_supported(const ProductArgs &a, int bits, int G)
 {
     XrPlan plan;
+    int xc;
 #define QMM_XR_CASE(B, GG) \
-    if (bits == B && G == GG) return plan_xr<B, GG>(a, plan);
+    if (bits == B && G == GG) return plan_xr_any<B, GG>(a, plan, xc);
     QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)
     QMM_XR_CASE(5, 32) QMM_XR_CASE(5, 64) QMM_XR_CASE(5, 128)
     QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)
