@@ -7,9 +7,12 @@
 // keeping many wide, coalesced loads of packed codes in flight:
 //
 //  * a workgroup of 4 waves owns 4*RPW output rows; each wave owns RPW rows;
-//  * lane l of a wave takes groups l, l+64, ..., l+64*(SLOTS-1) of a row, so
-//    every load instruction of a wave reads 64 consecutive groups, one
-//    contiguous span of the row's stream (16-byte loads for 4-bit G = 32);
+//  * LPR lanes (64 or 32) share a row: lane l takes row l / LPR of a row
+//    group and groups l % LPR + LPR*s (s < SLOTS) of that row, so every load
+//    instruction of a wave reads 64/LPR rows of LPR consecutive groups, whole
+//    contiguous spans of the rows' streams (16-byte loads for 4-bit G = 32).
+//    LPR = 32 covers group counts that are odd multiples of 32 without idle
+//    lanes (160 groups: 5 slots of 32 instead of 3 slots of 64);
 //  * the (row, slot) tasks of a wave form one fully unrolled sequence with a
 //    ring of PD register stages: the loads of task t + PD are issued as soon
 //    as task t is consumed, and the first PD tasks are issued before the
@@ -35,16 +38,19 @@ constexpr int kRowsPerWave = 4;
 constexpr int kPrefetchRows = 1;  // rows of loads kept in flight per wave
 constexpr int kMaxChunkK = 8192;  // activations staged per pass: at most 16 KB of fp16
 
-template <int BITS, int G, int SLOTS, int RPW, int PD_ROWS>
+template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
     constexpr int NWG = G * BITS / 32;        // words per group
     constexpr int NPAIR = G / 2;              // fp16 pairs per group
     constexpr int UPG = G / 8;                // 8-activation units per group
-    constexpr int CHUNK_G = SLOTS * kWave;    // groups per staged chunk
+    constexpr int RPI = kWave / LPR;          // rows per load instruction
+    constexpr int RG = RPW / RPI;             // row groups per wave
+    constexpr int CHUNK_G = SLOTS * LPR;      // groups per staged chunk
     constexpr int ALIGN = gcd_int(4 * NWG, 16);
-    constexpr int TASKS = RPW * SLOTS;
+    constexpr int TASKS = RG * SLOTS;
     constexpr int PD = TASKS < PD_ROWS * SLOTS ? TASKS : PD_ROWS * SLOTS;  // tasks in flight
+    static_assert(RPW % RPI == 0, "a wave's rows come in whole row groups");
     constexpr int ROWS = kWaves * RPW;        // rows of the workgroup
     constexpr int XUNITS = CHUNK_G * UPG;                           // activation units per chunk
     constexpr int XPT = (XUNITS + kThreads - 1) / kThreads;         // ... per thread
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     const size_t wpr = (size_t)K * BITS / 32;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int rho = lane / LPR, lam = lane % LPR;  // row within a row group, lane within the row
     const int wg_row0 = blockIdx.x * ROWS;
     const int row0 = wg_row0 + wave * RPW;
 
@@ -73,15 +80,21 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     // 16-byte scale/bias staging needs 8-group alignment of every row span
     const bool sb_vector = Kg % 8 == 0 && gbeg % 8 == 0 && gend % 8 == 0;
 
-    // Row of each task (clamped so loads stay in bounds; results of rows >= N are dropped).
-    size_t rowoff[RPW];
+    // Rows of each row group: a wave-uniform base row and this lane's row
+    // offset from it (clamped so loads stay in bounds; results of rows >= N
+    // are dropped).
+    size_t rowbase[RG];
+    uint32_t rowlane[RG];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-        rowoff[r] = (size_t)min(row0 + r, N - 1);
+    for (int r = 0; r < RG; ++r) {
+        const int b = min(row0 + r * RPI, N - 1);
+        rowbase[r] = (size_t)b;
+        rowlane[r] = (uint32_t)(min(row0 + r * RPI + rho, N - 1) - b) * (uint32_t)(wpr * 4);
+    }
 
-    float acc[RPW];
+    float acc[RG];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+    for (int r = 0; r < RG; ++r)
         acc[r] = 0.f;
 
     struct Stage {
@@ -122,11 +135,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
         int lgroup[SLOTS];
 #pragma unroll
         for (int sl = 0; sl < SLOTS; ++sl)
-            lgroup[sl] = min(lane + sl * kWave, ng - 1);
+            lgroup[sl] = min(lam + sl * LPR, ng - 1);
         auto load = [&](Stage &st, int task) {
             const int r = task / SLOTS, sl = task % SLOTS;
-            const uint32_t *wbase = a.wq + rowoff[r] * wpr + (size_t)g0 * NWG;
-            load_words<NWG, ALIGN>(byte_offset(wbase, (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
+            const uint32_t *wbase = a.wq + rowbase[r] * wpr + (size_t)g0 * NWG;
+            load_words<NWG, ALIGN>(byte_offset(wbase, rowlane[r] + (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
         };
 #pragma unroll
         for (int t = 0; t < PD; ++t)
@@ -188,8 +201,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 #pragma unroll
             for (int j = 0; j < NWG; ++j)
                 pin_register(st.w[j]);
-            if (sl * kWave < ng) {
-                const int gl = lane + sl * kWave;
+            if (sl * LPR < ng) {
+                const int gl = lam + sl * LPR;
                 const int glc = min(gl, ng - 1);
                 half2_t q[NPAIR];
                 unpack_pairs<BITS, G>(st.w, q);
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                     P = __builtin_amdgcn_fdot2(q[4 * u + 2], half2_t{xv[4], xv[5]}, P, false);
                     P = __builtin_amdgcn_fdot2(q[4 * u + 3], half2_t{xv[6], xv[7]}, P, false);
                 }
-                const uint32_t sb = sbl[wave * RPW + r][glc];
+                const uint32_t sb = sbl[wave * RPW + r * RPI + rho][glc];
                 const float sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
                 const float bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
                 const float contrib = sc * P + bias * xsum[glc];
@@ -213,25 +226,46 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
         }
     }
 
+    // Row sums: a DPP sum inside each 16-lane row, then the 16-lane rows of
+    // each of the RPI rows of a row group are added in order.
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const float v = wave_sum(acc[r]);
-        if (lane == 0 && row0 + r < N)
-            yout[row0 + r] = v;
+    for (int r = 0; r < RG; ++r) {
+        const int v = __builtin_bit_cast(int, row16_sum(acc[r]));
+        float part[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            part[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16 * q));
+#pragma unroll
+        for (int p = 0; p < RPI; ++p) {
+            constexpr int QPR = LPR / 16;  // 16-lane rows per output row
+            float sum = part[p * QPR];
+#pragma unroll
+            for (int q = 1; q < QPR; ++q)
+                sum += part[p * QPR + q];
+            const int row = row0 + r * RPI + p;
+            if (lane == 0 && row < N)
+                yout[row] = sum;
+        }
     }
 }
 
-template <int BITS, int G, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows>
+template <int BITS, int G, int LPR, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows>
 hipError_t launch_qmv_slots(const ProductArgs &a, hipStream_t stream)
 {
     const int rows_per_block = kWaves * RPW;
     const dim3 grid((a.N + rows_per_block - 1) / rows_per_block, 1, a.split);
-    hipLaunchKernelGGL((qmv_kernel<BITS, G, SLOTS, RPW, PD_ROWS>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Slots per lane: enough to cover the K range (or slice) in one staged chunk
-// when it fits, capped by the chunk's LDS size.
+// Lanes per row and slots per lane: enough slots to cover the K range (or
+// slice) in one staged chunk when it fits, capped by the chunk's LDS size.
+// With 32 lanes per row a wave's rows form two row groups, both kept in
+// flight (measured: 12.7 us against 13.8 us with one in flight on the
+// 5120 x 17408 4-bit projection).
+// 32 lanes per row take group counts that leave more than half of a 64-lane
+// slot idle (an odd number of 32-group slots covers them exactly); even
+// numbers of 32-group slots are the 64-lane kernel.
 template <int BITS, int G>
 hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
 {
@@ -240,13 +274,23 @@ hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
     const int slice = a.split > 1 ? (Kg + a.split - 1) / a.split : Kg;
     int slots = (slice + kWave - 1) / kWave;
     slots = slots < 1 ? 1 : (slots > max_slots ? max_slots : slots);
+    const int half = (slice + 31) / 32;  // 32-group slots covering the slice
+    if (slice <= max_slots * kWave && half % 2 == 1) {
+        if (half == 1) return launch_qmv_slots<BITS, G, 32, 1, kRowsPerWave, 2>(a, stream);
+        if constexpr (2 * max_slots >= 3)
+            if (half == 3) return launch_qmv_slots<BITS, G, 32, 3, kRowsPerWave, 2>(a, stream);
+        if constexpr (2 * max_slots >= 5)
+            if (half == 5) return launch_qmv_slots<BITS, G, 32, 5, kRowsPerWave, 2>(a, stream);
+        if constexpr (2 * max_slots >= 7)
+            if (half == 7) return launch_qmv_slots<BITS, G, 32, 7, kRowsPerWave, 2>(a, stream);
+    }
     if constexpr (max_slots >= 4)
-        if (slots == 4) return launch_qmv_slots<BITS, G, 4>(a, stream);
+        if (slots == 4) return launch_qmv_slots<BITS, G, 64, 4>(a, stream);
     if constexpr (max_slots >= 3)
-        if (slots == 3) return launch_qmv_slots<BITS, G, 3>(a, stream);
+        if (slots == 3) return launch_qmv_slots<BITS, G, 64, 3>(a, stream);
     if constexpr (max_slots >= 2)
-        if (slots == 2) return launch_qmv_slots<BITS, G, 2>(a, stream);
-    return launch_qmv_slots<BITS, G, 1>(a, stream);
+        if (slots == 2) return launch_qmv_slots<BITS, G, 64, 2>(a, stream);
+    return launch_qmv_slots<BITS, G, 64, 1>(a, stream);
 }
 
 }  // namespace
