@@ -5,7 +5,9 @@ product on one MI355X, for the 27B-style dense MLP up projection
 One step = one qmm_forward call at each of M = 1, 4, 16 (three launches),
 every call reading its own copy of the packed weights, scales and biases:
 the copies rotate over more than 512 MB so that no call is served from the
-256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
+256 MB Infinity Cache. Inputs are resident in HBM before timing starts. The
+timed steps are captured once into a HIP graph (untimed) and replayed, so the
+host's per-call cost does not leave the GPU idle between launches.
 
 value = weight bytes streamed per step / step time, where weight bytes per
 call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
@@ -305,22 +307,40 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps
+    # The launches are replayed from HIP graphs: a Python call of the binding
+    # costs about as much host time as a one-row product takes on the GPU, so
+    # eager launches would measure the host. Capture is untimed.
+    def capture(fn, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    step_graph = capture(lambda i: step(), args.steps)
+
+    # timed region: exactly `steps` steps (one replay of the captured steps)
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
-        step()
+    step_graph.replay()
     t_stop.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    del step_graph
 
-    # per-cell launch durations (same rotation), for the roofline and the breakdown
+    # per-cell launch durations (same rotation, graph replay), for the roofline
+    # and the breakdown
     cells = {}
     reps = max(50, 2 * C)
     for M in CELLS_M:
-        ms = time_launches(lambda i, M=M: call(M, i), reps, stream)
+        g = capture(lambda i, M=M: call(M, i), reps)
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
+        del g
         algo = shape.weight_bytes + 2 * M * shape.K + 4 * M * shape.N
         cells[f"M{M}"] = {
             "kernel": qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G),
