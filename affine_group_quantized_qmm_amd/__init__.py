@@ -32,6 +32,7 @@ _lib = ctypes.CDLL(str(LIBRARY_PATH))
 _p, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _lib.qmm_pack.argtypes = [_p, _p, _i, _i, _i, _p]
 _lib.qmm_forward.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_forward_rowexact.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
 _lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
@@ -41,12 +42,13 @@ _lib.qmm_strerror.argtypes = [_i]
 _lib.qmm_strerror.restype = ctypes.c_char_p
 _lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
 _lib.qmm_kernel_name.restype = ctypes.c_char_p
-for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_splitk, _lib.qmm_forward_kernel,
-           _lib.qmm_validate):
+for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_splitk,
+           _lib.qmm_forward_kernel, _lib.qmm_validate):
     _f.restype = _i
 
-EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_splitk", "qmm_splitk_workspace_bytes",
-            "qmm_validate", "qmm_strerror", "qmm_kernel_name", "qmm_forward_kernel")
+EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_splitk",
+            "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
+            "qmm_forward_kernel")
 
 
 QMM_ERR_UNSUPPORTED = -9  # qmm_forward_kernel: the named kernel cannot run this shape
@@ -142,6 +144,19 @@ def qmm_forward(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Ten
                           out.data_ptr(), M, K, N, bits, G, _stream(x))
     if rc:
         raise QmmError(rc, "qmm_forward")
+    return out
+
+
+def qmm_forward_rowexact(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Tensor:
+    """qmm_forward whose every row is bitwise equal to the one-row call on that row."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    rc = _lib.qmm_forward_rowexact(x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+                                   biases.data_ptr(), out.data_ptr(), M, K, N, bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_rowexact")
     return out
 
 

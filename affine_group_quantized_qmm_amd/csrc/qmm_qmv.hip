@@ -36,9 +36,14 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerWave = 4;
 constexpr int kPrefetchRows = 1;  // rows of loads kept in flight per wave
-constexpr int kMaxChunkK = 8192;  // activations staged per pass: at most 16 KB of fp16
+constexpr int kMaxChunkK = 8192;  // activations staged per pass: at most 16 KB of fp16 ...
+constexpr int chunk_limit(int mr) { return mr == 1 ? kMaxChunkK : 2 * kMaxChunkK; }  // ... 32 KB for several rows
 
-template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS>
+// MR: activation rows per launch (M <= MR). Every row runs exactly the
+// arithmetic of the one-row launch (same lane-to-group map, same dot and
+// epilogue sequence, same reduction tree), so with the same LPR each row of
+// an MR-row result is bitwise equal to that row computed alone.
+template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
     constexpr int NWG = G * BITS / 32;        // words per group
@@ -52,17 +57,17 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     constexpr int PD = TASKS < PD_ROWS * SLOTS ? TASKS : PD_ROWS * SLOTS;  // tasks in flight
     static_assert(RPW % RPI == 0, "a wave's rows come in whole row groups");
     constexpr int ROWS = kWaves * RPW;        // rows of the workgroup
-    constexpr int XUNITS = CHUNK_G * UPG;                           // activation units per chunk
-    constexpr int XPT = (XUNITS + kThreads - 1) / kThreads;         // ... per thread
+    constexpr int XUNITS = CHUNK_G * UPG;                           // activation units per row and chunk
+    constexpr int XPT = (MR * XUNITS + kThreads - 1) / kThreads;    // ... of all rows, per thread
     constexpr int SBU = ROWS * CHUNK_G / 8;                         // 8-group scale units per chunk
     constexpr int SPT = (SBU + kThreads - 1) / kThreads;            // ... per thread
-    static_assert(CHUNK_G * G <= kMaxChunkK, "staged chunk too large");
+    static_assert(MR * CHUNK_G * G <= chunk_limit(MR), "staged chunk too large");
     static_assert(CHUNK_G % 8 == 0, "chunks hold whole 8-group scale units");
 
-    // Activations unit-major: xp[u][g] holds units u of group g, so the
-    // 64 lanes of a wave (consecutive groups) read consecutive 16-byte units.
-    __shared__ half8_t xp[UPG][CHUNK_G];
-    __shared__ float xsum[CHUNK_G];
+    // Activations unit-major: xp[m][u][g] holds unit u of group g of row m,
+    // so the lanes of a row (consecutive groups) read consecutive 16-byte units.
+    __shared__ half8_t xp[MR][UPG][CHUNK_G];
+    __shared__ float xsum[MR][CHUNK_G];
     __shared__ uint32_t sbl[ROWS][CHUNK_G];   // (scale, bias) fp16 pair per row and group
 
     const int K = a.K, N = a.N, Kg = K / G;
@@ -92,10 +97,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
         rowlane[r] = (uint32_t)(min(row0 + r * RPI + rho, N - 1) - b) * (uint32_t)(wpr * 4);
     }
 
-    float acc[RG];
+    float acc[MR][RG];
 #pragma unroll
-    for (int r = 0; r < RG; ++r)
-        acc[r] = 0.f;
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+            acc[m][r] = 0.f;
 
     struct Stage {
         uint32_t w[NWG];
@@ -107,11 +114,14 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 
         // 1. Activation and scale/bias loads first: they head the memory
         //    queue, so the workgroup can start computing as early as possible.
+        // unit v: row v / XUNITS (rows past M re-read row M-1), unit v % XUNITS
         half8_t xreg[XPT];
 #pragma unroll
         for (int t = 0; t < XPT; ++t) {
-            const int u = min((int)threadIdx.x + t * kThreads, ng * UPG - 1);
-            xreg[t] = *reinterpret_cast<const half8_t *>(a.x + (size_t)g0 * G + 8 * u);
+            const int v = min((int)threadIdx.x + t * kThreads, MR * XUNITS - 1);
+            const int m = min(v / XUNITS, a.M - 1);
+            const int u = min(v % XUNITS, ng * UPG - 1);
+            xreg[t] = *reinterpret_cast<const half8_t *>(a.x + (size_t)m * K + (size_t)g0 * G + 8 * u);
         }
         u32x4 sreg[SPT], breg[SPT];
         if (sb_vector) {
@@ -150,19 +160,21 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
         __syncthreads();  // all waves are done reading the previous chunk
 #pragma unroll
         for (int t = 0; t < XPT; ++t) {
-            const int u = (int)threadIdx.x + t * kThreads;
+            const int vv = (int)threadIdx.x + t * kThreads;
+            const int m = vv / XUNITS, u = vv % XUNITS;
             const half8_t v = xreg[t];
             float s8 = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 s8 += (float)v[e];
+            // the UPG units of a group sit in consecutive lanes
 #pragma unroll
             for (int off = 1; off < UPG; off *= 2)
                 s8 += __shfl_xor(s8, off);
-            if (u < ng * UPG) {
-                xp[u % UPG][u / UPG] = to_pair_order<BITS>(v);
+            if (m < MR && u < ng * UPG) {
+                xp[m][u % UPG][u / UPG] = to_pair_order<BITS>(v);
                 if (u % UPG == 0)
-                    xsum[u / UPG] = s8;
+                    xsum[m][u / UPG] = s8;
             }
         }
         if (sb_vector) {
@@ -206,20 +218,24 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                 const int glc = min(gl, ng - 1);
                 half2_t q[NPAIR];
                 unpack_pairs<BITS, G>(st.w, q);
-                float P = 0.f;
-#pragma unroll
-                for (int u = 0; u < UPG; ++u) {
-                    const half8_t xv = xp[u][glc];
-                    P = __builtin_amdgcn_fdot2(q[4 * u + 0], half2_t{xv[0], xv[1]}, P, false);
-                    P = __builtin_amdgcn_fdot2(q[4 * u + 1], half2_t{xv[2], xv[3]}, P, false);
-                    P = __builtin_amdgcn_fdot2(q[4 * u + 2], half2_t{xv[4], xv[5]}, P, false);
-                    P = __builtin_amdgcn_fdot2(q[4 * u + 3], half2_t{xv[6], xv[7]}, P, false);
-                }
                 const uint32_t sb = sbl[wave * RPW + r * RPI + rho][glc];
                 const float sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
                 const float bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
-                const float contrib = sc * P + bias * xsum[glc];
-                acc[r] += gl < ng ? contrib : 0.f;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float P = 0.f;
+#pragma unroll
+                    for (int u = 0; u < UPG; ++u) {
+                        const half8_t xv = xp[m][u][glc];
+                        P = __builtin_amdgcn_fdot2(q[4 * u + 0], half2_t{xv[0], xv[1]}, P, false);
+                        P = __builtin_amdgcn_fdot2(q[4 * u + 1], half2_t{xv[2], xv[3]}, P, false);
+                        P = __builtin_amdgcn_fdot2(q[4 * u + 2], half2_t{xv[4], xv[5]}, P, false);
+                        P = __builtin_amdgcn_fdot2(q[4 * u + 3], half2_t{xv[6], xv[7]}, P, false);
+                    }
+                    // explicit fma: the same rounding in every instantiation
+                    const float contrib = __builtin_fmaf(sc, P, bias * xsum[m][glc]);
+                    acc[m][r] += gl < ng ? contrib : 0.f;
+                }
             }
             if (t + PD < TASKS)
                 load(ring[t % PD], t + PD);
@@ -229,68 +245,118 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     // Row sums: a DPP sum inside each 16-lane row, then the 16-lane rows of
     // each of the RPI rows of a row group are added in order.
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-        const int v = __builtin_bit_cast(int, row16_sum(acc[r]));
-        float part[4];
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            part[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16 * q));
+        for (int r = 0; r < RG; ++r) {
+            const int v = __builtin_bit_cast(int, row16_sum(acc[m][r]));
+            float part[4];
 #pragma unroll
-        for (int p = 0; p < RPI; ++p) {
-            constexpr int QPR = LPR / 16;  // 16-lane rows per output row
-            float sum = part[p * QPR];
+            for (int q = 0; q < 4; ++q)
+                part[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16 * q));
 #pragma unroll
-            for (int q = 1; q < QPR; ++q)
-                sum += part[p * QPR + q];
-            const int row = row0 + r * RPI + p;
-            if (lane == 0 && row < N)
-                yout[row] = sum;
+            for (int p = 0; p < RPI; ++p) {
+                constexpr int QPR = LPR / 16;  // 16-lane rows per output row
+                float sum = part[p * QPR];
+#pragma unroll
+                for (int q = 1; q < QPR; ++q)
+                    sum += part[p * QPR + q];
+                const int row = row0 + r * RPI + p;
+                if (lane == 0 && row < N && m < a.M)
+                    yout[(size_t)m * N + row] = sum;
+            }
         }
     }
 }
 
-template <int BITS, int G, int LPR, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows>
+template <int BITS, int G, int LPR, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows, int MR = 1>
 hipError_t launch_qmv_slots(const ProductArgs &a, hipStream_t stream)
 {
     const int rows_per_block = kWaves * RPW;
     const dim3 grid((a.N + rows_per_block - 1) / rows_per_block, 1, a.split);
-    hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS, MR>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Lanes per row and slots per lane: enough slots to cover the K range (or
-// slice) in one staged chunk when it fits, capped by the chunk's LDS size.
-// With 32 lanes per row a wave's rows form two row groups, both kept in
-// flight (measured: 12.7 us against 13.8 us with one in flight on the
-// 5120 x 17408 4-bit projection).
-// 32 lanes per row take group counts that leave more than half of a 64-lane
-// slot idle (an odd number of 32-group slots covers them exactly); even
-// numbers of 32-group slots are the 64-lane kernel.
+// Lanes per row: 32 for group counts that leave more than half of a 64-lane
+// slot idle (an odd number of 32-group slots covers them exactly), else 64.
+// The choice depends on the K range only, so every row count takes the same
+// lane map as the one-row launch. Slots per lane: enough to cover the range
+// in one staged chunk when the chunk of all MR rows fits (chunk_limit(MR)
+// activations), else as many as fit.
+template <int BITS, int G>
+int qmv_lanes_per_row(int slice)
+{
+    constexpr int max_slots1 = kMaxChunkK / (kWave * G);
+    const int half = (slice + 31) / 32;
+    return slice <= max_slots1 * kWave && half % 2 == 1 ? 32 : 64;
+}
+
+template <int BITS, int G, int LPR, int MR, int S>
+hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
+{
+    // PD: with 32 lanes per row both row groups of a wave stay in flight
+    // (measured: 12.7 us against 13.8 us with one on the 5120 x 17408 4-bit
+    // projection at M = 1).
+    constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
+    if constexpr (S > 1) {
+        if (slots >= S)
+            return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR>(a, stream);
+        return launch_qmv_upto<BITS, G, LPR, MR, S - 1>(a, slots, stream);
+    } else {
+        return launch_qmv_slots<BITS, G, LPR, 1, kRowsPerWave, PDR, MR>(a, stream);
+    }
+}
+
+template <int BITS, int G, int MR>
+hipError_t launch_qmv_rows(const ProductArgs &a, hipStream_t stream)
+{
+    const int Kg = a.K / G;
+    const int slice = a.split > 1 ? (Kg + a.split - 1) / a.split : Kg;
+    const int lpr = qmv_lanes_per_row<BITS, G>(slice);
+    const int need = (slice + lpr - 1) / lpr;
+    if (lpr == 32) {
+        constexpr int max_s = chunk_limit(MR) / (MR * 32 * G);
+        if constexpr (max_s >= 1)
+            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8)>(a, need, stream);
+    } else {
+        constexpr int max_s = chunk_limit(MR) / (MR * 64 * G);
+        if constexpr (max_s >= 1)
+            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4)>(a, need, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Rows per launch that fit a one-slot chunk with this lane map.
+template <int BITS, int G>
+int qmv_max_rows(int lpr)
+{
+    int mr = 8;
+    while (mr > 1 && chunk_limit(mr) / (mr * lpr * G) < 1)
+        mr /= 2;
+    return mr;
+}
+
+// Up to 8 rows (a.M <= 8), in as few launches as the chunk size allows.
 template <int BITS, int G>
 hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
 {
-    constexpr int max_slots = kMaxChunkK / (kWave * G);
     const int Kg = a.K / G;
     const int slice = a.split > 1 ? (Kg + a.split - 1) / a.split : Kg;
-    int slots = (slice + kWave - 1) / kWave;
-    slots = slots < 1 ? 1 : (slots > max_slots ? max_slots : slots);
-    const int half = (slice + 31) / 32;  // 32-group slots covering the slice
-    if (slice <= max_slots * kWave && half % 2 == 1) {
-        if (half == 1) return launch_qmv_slots<BITS, G, 32, 1, kRowsPerWave, 2>(a, stream);
-        if constexpr (2 * max_slots >= 3)
-            if (half == 3) return launch_qmv_slots<BITS, G, 32, 3, kRowsPerWave, 2>(a, stream);
-        if constexpr (2 * max_slots >= 5)
-            if (half == 5) return launch_qmv_slots<BITS, G, 32, 5, kRowsPerWave, 2>(a, stream);
-        if constexpr (2 * max_slots >= 7)
-            if (half == 7) return launch_qmv_slots<BITS, G, 32, 7, kRowsPerWave, 2>(a, stream);
+    const int cap = qmv_max_rows<BITS, G>(qmv_lanes_per_row<BITS, G>(slice));
+    ProductArgs b = a;
+    for (int m0 = 0; m0 < a.M; m0 += cap) {
+        b.M = a.M - m0 < cap ? a.M - m0 : cap;
+        b.x = a.x + (size_t)m0 * a.K;
+        b.y = a.y + (size_t)m0 * a.N;
+        hipError_t e;
+        if (b.M <= 1) e = launch_qmv_rows<BITS, G, 1>(b, stream);
+        else if (b.M <= 2) e = launch_qmv_rows<BITS, G, 2>(b, stream);
+        else if (b.M <= 4) e = launch_qmv_rows<BITS, G, 4>(b, stream);
+        else e = launch_qmv_rows<BITS, G, 8>(b, stream);
+        if (e != hipSuccess)
+            return e;
     }
-    if constexpr (max_slots >= 4)
-        if (slots == 4) return launch_qmv_slots<BITS, G, 64, 4>(a, stream);
-    if constexpr (max_slots >= 3)
-        if (slots == 3) return launch_qmv_slots<BITS, G, 64, 3>(a, stream);
-    if constexpr (max_slots >= 2)
-        if (slots == 2) return launch_qmv_slots<BITS, G, 64, 2>(a, stream);
-    return launch_qmv_slots<BITS, G, 64, 1>(a, stream);
+    return hipSuccess;
 }
 
 }  // namespace

@@ -123,6 +123,17 @@ int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *sc
                        int G, int split_k, float *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* Row-exact product (vmlx-swift pull request #565 page, commit introducing
+ * qwen_qmv_rows_full: every verify row keeps the one-row kernel's statement
+ * order, so a multi-row call reproduces the one-row results bit for bit).
+ * Same arguments, layout, ownership and errors as qmm_forward; every row m of
+ * y is bitwise equal to qmm_forward on row m alone (M = 1) with the same K,
+ * N, bits and G. Runs the one-row VALU kernel on up to 8 rows per launch
+ * (the weights are read once per 8 rows). Async on `stream`. */
+int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                         const uint16_t *biases, float *y, int M, int K, int N, int bits,
+                         int G, hipStream_t stream);
+
 /* Bytes of workspace qmm_forward_splitk needs: split_k * M * N * 4 for
  * split_k >= 2, 0 for split_k == 1 and for invalid arguments. */
 size_t qmm_splitk_workspace_bytes(int M, int N, int split_k);
@@ -144,15 +155,15 @@ const char *qmm_kernel_name(int M, int K, int N, int bits, int G);
 
 /* qmm_forward with the kernel named explicitly instead of chosen from M
  * (a test and benchmark aid):
- *   "qmv"      the one-row mat-vec, once per activation row (streaming the
- *              weights M times); qmm_forward's choice for M == 1;
+ *   "qmv"      the row-exact VALU kernel (qmm_forward_rowexact), up to 8
+ *              rows per launch; qmm_forward's choice for M <= 2;
  *   "mfma"     the multi-row matrix-core kernel with each wave's K part of
- *              the activations in registers; qmm_forward's choice for M >= 2
+ *              the activations in registers; qmm_forward's choice for M >= 3
  *              when the shape allows it (K * bits a multiple of 128 and K
  *              short enough for 8 parts of 768 activations, 512 for 8-bit
  *              codes); QMM_ERR_UNSUPPORTED otherwise;
  *   "mfma_lds" the multi-row matrix-core kernel that streams activations
- *              through LDS; any shape; qmm_forward's choice for M >= 2 when
+ *              through LDS; any shape; qmm_forward's choice for M >= 3 when
  *              "mfma" does not apply.
  * Same arguments, layout and errors as qmm_forward; an unknown name returns
  * QMM_ERR_SHAPE, a NULL name QMM_ERR_NULL. */

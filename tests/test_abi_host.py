@@ -79,12 +79,14 @@ def test_validation_rejects(kw, code):
 
 def test_kernel_choice():
     assert qmm.qmm_kernel_name(1, 5120, 17408, 4, 32) == "qmv"
+    assert qmm.qmm_kernel_name(2, 5120, 17408, 4, 32) == "qmv"
+    assert qmm.qmm_kernel_name(3, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 3, 32) is None
     # activations of K = 17408 do not fit 8 parts of 768: the LDS-streaming kernel
     assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma_lds"
-    assert qmm.qmm_kernel_name(2, 6144, 1024, 4, 32) == "mfma"
-    assert qmm.qmm_kernel_name(2, 6176, 1024, 4, 32) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 6144, 1024, 4, 32) == "mfma"
+    assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma_lds"
     # 5-bit rows of 13 groups are not whole 16-byte units
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma_lds"

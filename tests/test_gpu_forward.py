@@ -38,7 +38,7 @@ def run_kernel(kernel, dp, bits, G):
     except qmm.QmmError as e:
         assert kernel == "mfma" and e.code == qmm.QMM_ERR_UNSUPPORTED, str(e)
         M, K, N = dp.p.M, dp.p.K, dp.p.N
-        assert qmm.qmm_kernel_name(max(M, 2), K, N, bits, G) == "mfma_lds"
+        assert qmm.qmm_kernel_name(max(M, 3), K, N, bits, G) == "mfma_lds"
         return None
 
 
