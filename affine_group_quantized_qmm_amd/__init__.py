@@ -35,6 +35,7 @@ _lib.qmm_forward.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_rowexact.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
 _lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_forward_fused.argtypes = [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
 _lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.qmm_splitk_workspace_bytes.restype = _sz
 _lib.qmm_validate.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz]
@@ -43,12 +44,14 @@ _lib.qmm_strerror.restype = ctypes.c_char_p
 _lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
 _lib.qmm_kernel_name.restype = ctypes.c_char_p
 for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_splitk,
-           _lib.qmm_forward_kernel, _lib.qmm_validate):
+           _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_validate):
     _f.restype = _i
 
 EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_splitk",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
-            "qmm_forward_kernel")
+            "qmm_forward_kernel", "qmm_forward_fused")
+
+QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 
 
 QMM_ERR_UNSUPPORTED = -9  # qmm_forward_kernel: the named kernel cannot run this shape
@@ -158,6 +161,39 @@ def qmm_forward_rowexact(x, wq, scales, biases, bits: int, G: int, out=None) -> 
     if rc:
         raise QmmError(rc, "qmm_forward_rowexact")
     return out
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def qmm_forward_fused(x, projections, bits: int, G: int, outs=None) -> list[torch.Tensor]:
+    """Several projections of the same x in one launch.
+
+    `projections` is a sequence of (wq, scales, biases) triples with a common K;
+    returns one fp32 [M, N_p] tensor per projection (or fills `outs`)."""
+    count = len(projections)
+    if count < 1:
+        raise ValueError("at least one projection")
+    dims = [_operands(x, wq, s, b, bits, G) for wq, s, b in projections]
+    M, K, _, dev = dims[0]
+    Ns = [d[2] for d in dims]
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.float32, device=dev) for n in Ns]
+    if len(outs) != count:
+        raise ValueError("one output per projection")
+    for o, n in zip(outs, Ns):
+        _check(o, "out", (torch.float32,), (M, n), dev)
+    rc = _lib.qmm_forward_fused(
+        x.data_ptr(), count,
+        _ptr_array([p[0].data_ptr() for p in projections]),
+        _ptr_array([p[1].data_ptr() for p in projections]),
+        _ptr_array([p[2].data_ptr() for p in projections]),
+        _ptr_array([o.data_ptr() for o in outs]),
+        (ctypes.c_int * count)(*Ns), M, K, bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_fused")
+    return outs
 
 
 def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,

@@ -11,6 +11,7 @@ namespace {
 constexpr int kMaxRowsPerLaunch = 16;  // rows of one multi-row launch (one MFMA tile)
 constexpr int kQmvRowsPerLaunch = 8;   // rows of one launch of the row-exact VALU kernel
 constexpr int kQmvMaxRows = 2;         // qmm_forward takes the VALU kernel up to this many rows
+static_assert(QMM_MAX_FUSED <= qmm::kMaxProj, "the launch arguments hold every fused projection");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -77,18 +78,14 @@ Kernel choose_kernel(int M, int K, int N, int bits, int G, int split)
 
 // Launch one product (all of M, in 16-row steps for the multi-row kernels)
 // writing either y (split == 1) or the split partials (y = workspace).
-int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
-                   const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
-                   int split, hipStream_t stream)
+int launch_args(Kernel kind, const qmm::ProductArgs &full, int bits, int G, hipStream_t stream)
 {
-    if (kind == Kernel::mfma && !xr_supported(K, N, bits, G, split))
+    if (kind == Kernel::mfma && !xr_supported(full.K, full.N, bits, G, full.split))
         return QMM_ERR_UNSUPPORTED;
-    qmm::ProductArgs a = product_args(x, wq, scales, biases, y, M, K, N, split);
+    const int M = full.M;
     const int step = kind == Kernel::qmv ? kQmvRowsPerLaunch : kMaxRowsPerLaunch;
     for (int m0 = 0; m0 < M; m0 += step) {
-        a.M = M - m0 < step ? M - m0 : step;
-        a.x = x + (size_t)m0 * K;
-        a.y = y + (size_t)m0 * N;
+        const qmm::ProductArgs a = qmm::rows_of(full, m0, M - m0 < step ? M - m0 : step);
         hipError_t e;
         switch (kind) {
         case Kernel::qmv: e = qmm::launch_qmv(a, bits, G, stream); break;
@@ -99,6 +96,13 @@ int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uin
             return QMM_ERR_LAUNCH;
     }
     return QMM_OK;
+}
+
+int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                   const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
+                   int split, hipStream_t stream)
+{
+    return launch_args(kind, product_args(x, wq, scales, biases, y, M, K, N, split), bits, G, stream);
 }
 
 }  // namespace
@@ -211,6 +215,36 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
     if (rc != QMM_OK)
         return rc;
     return launch_product(Kernel::qmv, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
+}
+
+int qmm_forward_fused(const uint16_t *x, int count, const uint32_t *const *wq,
+                      const uint16_t *const *scales, const uint16_t *const *biases, float *const *y,
+                      const int *N, int M, int K, int bits, int G, hipStream_t stream)
+{
+    if (!x || !wq || !scales || !biases || !y || !N)
+        return QMM_ERR_NULL;
+    if (count < 1 || count > QMM_MAX_FUSED)
+        return QMM_ERR_SHAPE;
+    qmm::ProductArgs a = product_args(x, nullptr, nullptr, nullptr, nullptr, M, K, 0, 1);
+    a.nproj = count;
+    int tiles = 0;
+    for (int p = 0; p < count; ++p) {
+        const int rc = qmm_validate(x, wq[p], scales[p], biases[p], y[p], M, K, N[p], bits, G, 0,
+                                    nullptr, 0);
+        if (rc != QMM_OK)
+            return rc;
+        a.tile0[p] = tiles;
+        a.proj[p] = qmm::Proj{wq[p], scales[p], biases[p], y[p], N[p]};
+        tiles += (N[p] + 15) / 16;
+        if (tiles >= (1 << 26))
+            return QMM_ERR_SHAPE;
+    }
+    a.tile0[count] = tiles;
+    if (count == 1)  // the plain single-projection launch
+        return launch_product(choose_kernel(M, K, N[0], bits, G, 1), x, wq[0], scales[0], biases[0],
+                              y[0], M, K, N[0], bits, G, 1, stream);
+    a.N = 16 * tiles;  // the launch's row space: every projection padded to whole tiles
+    return launch_args(choose_kernel(M, K, a.N, bits, G, 1), a, bits, G, stream);
 }
 
 int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,

@@ -8,11 +8,28 @@
 
 namespace qmm {
 
+constexpr int kMaxProj = 4;  // projections sharing x in one fused launch
+
+// One weight matrix with its output: codes, scales, biases, y [M, N].
+struct Proj {
+    const uint32_t *wq;
+    const uint16_t *scales;
+    const uint16_t *biases;
+    float *y;
+    int N;
+};
+
 // Arguments of one product launch. `y` receives either the final result
 // (split == 1) or slice z's partial product at y + z*y_slice_stride
 // (split > 1). M is the number of activation rows of this launch; the
 // multi-row kernel takes at most 16 and the host walks larger M in 16-row
 // steps.
+//
+// Fused launches (nproj >= 2, split == 1) run several projections of the
+// same x: projection p owns the 16-row tiles [tile0[p], tile0[p+1]) of the
+// launch, its rows padded to whole tiles, and N is 16 * tile0[nproj]. Every
+// kernel works in 16-row tiles (a workgroup or a K-part wave owns whole
+// tiles), so each tile belongs to one projection.
 struct ProductArgs {
     const uint16_t *x;
     const uint32_t *wq;
@@ -22,7 +39,40 @@ struct ProductArgs {
     int M, K, N;
     int split;               // number of K slices (grid z); 1 = whole K
     size_t y_slice_stride;   // elements between consecutive slices' partials in y
+    int nproj;               // 0 or 1: the single projection above
+    int tile0[kMaxProj + 1];
+    Proj proj[kMaxProj];
 };
+
+// The projection that owns 16-row tile t of a launch, and t's index inside it.
+struct Slab {
+    Proj p;
+    int tile;
+};
+
+__host__ __device__ __forceinline__ Slab slab_of_tile(const ProductArgs &a, int t)
+{
+    if (a.nproj <= 1)
+        return Slab{Proj{a.wq, a.scales, a.biases, a.y, a.N}, t};
+    int q = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxProj; ++j)
+        q = (j < a.nproj && t >= a.tile0[j]) ? j : q;
+    return Slab{a.proj[q], t - a.tile0[q]};
+}
+
+// Rows [m0, m0 + count) of a launch: x and every output advance by m0 rows.
+inline ProductArgs rows_of(const ProductArgs &a, int m0, int count)
+{
+    ProductArgs b = a;
+    b.M = count;
+    b.x = a.x + (size_t)m0 * a.K;
+    if (a.y)  // NULL in fused launches, whose outputs are the projections'
+        b.y = a.y + (size_t)m0 * a.N;
+    for (int j = 0; j < a.nproj && j < kMaxProj; ++j)
+        b.proj[j].y = a.proj[j].y + (size_t)m0 * a.proj[j].N;
+    return b;
+}
 
 // Each launcher returns a hipError_t from the launch (hipSuccess, or the
 // runtime's error) and hipErrorInvalidValue for an unsupported (bits, G).

@@ -137,7 +137,8 @@ void mfma_kernel(const ProductArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int rt = wave % RT, kp = wave / RT;
     const int c = lane / 16, i = lane % 16;
-    const int M = a.M, K = a.K, N = a.N, Kg = K / G;
+    const Slab slab = slab_of_tile(a, (int)blockIdx.x * RT + rt);  // the projection of this wave's tile
+    const int M = a.M, K = a.K, N = slab.p.N, Kg = K / G;
     const size_t wpr = (size_t)K * BITS / 32;
 
     int gb = 0, ge = Kg;
@@ -155,10 +156,10 @@ void mfma_kernel(const ProductArgs a)
     const int nchunks = ((ge - gb + KP - 1) / KP + CG - 1) / CG;  // same for every wave
 
     // weight row of this lane (clamped so every load stays in bounds)
-    const size_t n = (size_t)min((int)blockIdx.x * RT * 16 + rt * 16 + i, N - 1);
-    const uint32_t *wrow = a.wq + n * wpr + (Geo::kTranspose ? (size_t)c * NWG : (size_t)((c * Geo::CHB) / 32));
-    const uint16_t *srow = a.scales + n * Kg + (Geo::kTranspose ? c : 0);
-    const uint16_t *brow = a.biases + n * Kg + (Geo::kTranspose ? c : 0);
+    const size_t n = (size_t)min(slab.tile * 16 + i, N - 1);
+    const uint32_t *wrow = slab.p.wq + n * wpr + (Geo::kTranspose ? (size_t)c * NWG : (size_t)((c * Geo::CHB) / 32));
+    const uint16_t *srow = slab.p.scales + n * Kg + (Geo::kTranspose ? c : 0);
+    const uint16_t *brow = slab.p.biases + n * Kg + (Geo::kTranspose ? c : 0);
     const int chunk_shift = (c * Geo::CHB) % 32;  // direct path
 
     // Activation staging: unit u is part p = u / PART_UNITS, row
@@ -324,8 +325,8 @@ void mfma_kernel(const ProductArgs a)
         red[kp][rt][r][lane] = acc[r];
     __syncthreads();
     if (kp == 0) {
-        const int col = (int)blockIdx.x * RT * 16 + rt * 16 + i;
-        float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
+        const int col = slab.tile * 16 + i;
+        float *__restrict__ yout = slab.p.y + (size_t)blockIdx.z * a.y_slice_stride;
 #pragma unroll
         for (int r = 0; r < RLIVE; ++r) {
             float v = red[0][rt][r][lane];

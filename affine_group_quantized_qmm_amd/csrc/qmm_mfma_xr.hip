@@ -113,7 +113,8 @@ __host__ __device__ constexpr size_t xr_lds_bytes(int KP)
 
 // SBW: bytes per scale/bias load (4: two groups per load, 2: one group).
 // NST: tiles of loads in flight per wave (register stages).
-template <int BITS, int G, int XC, int SBW, int NST>
+// FUSED: the launch runs several projections (tile -> projection lookup).
+template <int BITS, int G, int XC, int SBW, int NST, bool FUSED>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
     using Geo = XrGeo<BITS, G, XC>;
@@ -136,7 +137,14 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
     };
     const int c = lane / 16, i = lane % 16;
-    const int M = a.M, K = a.K, N = a.N, Kg = K / G;
+    const int M = a.M, K = a.K, Kg = K / G;
+    // projection of a tile; single-projection launches skip the lookup
+    auto slab_at = [&](int t) -> Slab {
+        if constexpr (FUSED)
+            return slab_of_tile(a, t);
+        else
+            return Slab{Proj{a.wq, a.scales, a.biases, a.y, a.N}, t};
+    };
     const uint32_t RB = (uint32_t)K * BITS / 8;  // bytes per weight row
 
     int gb = 0, ge = Kg;
@@ -183,24 +191,24 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         // loads makes the compiler drain every load in flight
         uint32_t keep = tile >= t1 ? 0u : ~0u;
         pin_register(keep);
-        tile = min(tile, t1 - 1);
-        const int rmax = N - 1 - tile * 16;  // rows past N re-read row N-1
-        const uint8_t *wt = reinterpret_cast<const uint8_t *>(a.wq) + (size_t)tile * 16 * RB;
+        const Slab sl = slab_at(min(tile, t1 - 1));
+        const int rmax = sl.p.N - 1 - sl.tile * 16;  // rows past N re-read row N-1
+        const uint8_t *wt = reinterpret_cast<const uint8_t *>(sl.p.wq) + (size_t)sl.tile * 16 * RB;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const uint32_t off = ((uint32_t)min(wr[j], rmax) * RB + wcol[j]) & keep;
             st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(wt + off));
         }
-        const size_t sbase = (size_t)tile * 16 * Kg + pb;
+        const size_t sbase = (size_t)sl.tile * 16 * Kg + pb;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             const uint32_t off = ((uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE) & keep;
             if constexpr (SBW == 4) {
-                st.s[j] = *reinterpret_cast<const uint32_t *>(a.scales + sbase + off);
-                st.b[j] = *reinterpret_cast<const uint32_t *>(a.biases + sbase + off);
+                st.s[j] = *reinterpret_cast<const uint32_t *>(sl.p.scales + sbase + off);
+                st.b[j] = *reinterpret_cast<const uint32_t *>(sl.p.biases + sbase + off);
             } else {
-                st.s[j] = a.scales[sbase + off];
-                st.b[j] = a.biases[sbase + off];
+                st.s[j] = sl.p.scales[sbase + off];
+                st.b[j] = sl.p.biases[sbase + off];
             }
         }
     };
@@ -282,7 +290,6 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     const int chunk_shift = 8 * (chunk_byte % 4);
     const uint8_t *wrow_lds = wmy + i * LSTR + (chunk_byte & ~3);
     const uint32_t *sbrow = sbmy + i * SBSTR;
-    float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
 
     auto process = [&](Stage &sk, int tile) {
         __builtin_amdgcn_sched_barrier(0);
@@ -354,7 +361,9 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
             __syncthreads();
             const int first = tile - slot;
             for (int sl = kp; sl <= slot; sl += KP) {
-                const int col = (first + sl) * 16 + i;
+                const Slab ts = slab_at(first + sl);
+                const int col = ts.tile * 16 + i, N = ts.p.N;
+                float *__restrict__ yout = ts.p.y + (size_t)blockIdx.z * a.y_slice_stride;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float v = red_at(buf, sl, 0, r);
@@ -449,19 +458,29 @@ hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream
     static bool allowed = false;
     if (!allowed) {
         const int cap = (int)xr_lds_bytes<BITS, G, XC>(kXrMaxParts);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-        if (e != hipSuccess)
-            return e;
+        const void *fns[4] = {reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false>),
+                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false>),
+                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, true>),
+                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, true>)};
+        for (const void *f : fns) {
+            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+            if (e != hipSuccess)
+                return e;
+        }
         allowed = true;
     }
-    if (plan.sbw == 4)
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4>), grid, block, lds, stream, xa);
-    else
-        hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2>), grid, block, lds, stream, xa);
+    const bool fused = a.nproj >= 2;
+    if (plan.sbw == 4) {
+        if (fused)
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, true>), grid, block, lds, stream, xa);
+        else
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false>), grid, block, lds, stream, xa);
+    } else {
+        if (fused)
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, true>), grid, block, lds, stream, xa);
+        else
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false>), grid, block, lds, stream, xa);
+    }
     return hipGetLastError();
 }
 

@@ -70,18 +70,20 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     __shared__ float xsum[MR][CHUNK_G];
     __shared__ uint32_t sbl[ROWS][CHUNK_G];   // (scale, bias) fp16 pair per row and group
 
-    const int K = a.K, N = a.N, Kg = K / G;
+    static_assert(ROWS == 16, "a workgroup owns one 16-row tile");
+    const Slab slab = slab_of_tile(a, blockIdx.x);  // the projection of this workgroup's tile
+    const int K = a.K, N = slab.p.N, Kg = K / G;
     const size_t wpr = (size_t)K * BITS / 32;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int rho = lane / LPR, lam = lane % LPR;  // row within a row group, lane within the row
-    const int wg_row0 = blockIdx.x * ROWS;
+    const int wg_row0 = slab.tile * ROWS;
     const int row0 = wg_row0 + wave * RPW;
 
     int gbeg = 0, gend = Kg;
     if (a.split > 1)
         slice_groups(Kg, a.split, blockIdx.z, gbeg, gend);
-    float *__restrict__ yout = a.y + (size_t)blockIdx.z * a.y_slice_stride;
+    float *__restrict__ yout = slab.p.y + (size_t)blockIdx.z * a.y_slice_stride;
     // 16-byte scale/bias staging needs 8-group alignment of every row span
     const bool sb_vector = Kg % 8 == 0 && gbeg % 8 == 0 && gend % 8 == 0;
 
@@ -132,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                 const int r = v / (CHUNK_G / 8);
                 const int gu = min(8 * (v % (CHUNK_G / 8)), ng - 8);
                 const size_t off = (size_t)min(wg_row0 + r, N - 1) * Kg + g0 + gu;
-                sreg[t] = *reinterpret_cast<const u32x4 *>(a.scales + off);
-                breg[t] = *reinterpret_cast<const u32x4 *>(a.biases + off);
+                sreg[t] = *reinterpret_cast<const u32x4 *>(slab.p.scales + off);
+                breg[t] = *reinterpret_cast<const u32x4 *>(slab.p.biases + off);
             }
         }
 
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             lgroup[sl] = min(lam + sl * LPR, ng - 1);
         auto load = [&](Stage &st, int task) {
             const int r = task / SLOTS, sl = task % SLOTS;
-            const uint32_t *wbase = a.wq + rowbase[r] * wpr + (size_t)g0 * NWG;
+            const uint32_t *wbase = slab.p.wq + rowbase[r] * wpr + (size_t)g0 * NWG;
             load_words<NWG, ALIGN>(byte_offset(wbase, rowlane[r] + (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
         };
 #pragma unroll
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             for (int v = threadIdx.x; v < ROWS * ng; v += kThreads) {
                 const int r = v / ng, gl = v % ng;
                 const size_t off = (size_t)min(wg_row0 + r, N - 1) * Kg + g0 + gl;
-                sbl[r][gl] = (uint32_t)a.scales[off] | ((uint32_t)a.biases[off] << 16);
+                sbl[r][gl] = (uint32_t)slab.p.scales[off] | ((uint32_t)slab.p.biases[off] << 16);
             }
         }
         __syncthreads();
@@ -343,11 +345,8 @@ hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
     const int Kg = a.K / G;
     const int slice = a.split > 1 ? (Kg + a.split - 1) / a.split : Kg;
     const int cap = qmv_max_rows<BITS, G>(qmv_lanes_per_row<BITS, G>(slice));
-    ProductArgs b = a;
     for (int m0 = 0; m0 < a.M; m0 += cap) {
-        b.M = a.M - m0 < cap ? a.M - m0 : cap;
-        b.x = a.x + (size_t)m0 * a.K;
-        b.y = a.y + (size_t)m0 * a.N;
+        const ProductArgs b = rows_of(a, m0, a.M - m0 < cap ? a.M - m0 : cap);
         hipError_t e;
         if (b.M <= 1) e = launch_qmv_rows<BITS, G, 1>(b, stream);
         else if (b.M <= 2) e = launch_qmv_rows<BITS, G, 2>(b, stream);

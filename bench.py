@@ -12,7 +12,10 @@ host's per-call cost does not leave the GPU idle between launches.
 value = weight bytes streamed per step / step time, where weight bytes per
 call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 
-Prints one JSON line. Synthetic data (seeded; no trained weights).
+Prints one JSON line. Synthetic data (seeded; no trained weights). Besides
+the headline cells the line carries `layer`: one decoder layer of the layer
+sweep at M = 1 and 8, its seven projections launched one by one and with
+q/k/v and gate/up fused (qmm_forward_fused).
 
 The roofline object covers the kernel that takes most of a step. Its
 `traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE and
@@ -68,6 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the decoder-layer cell (separate vs fused projections)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="output rows of the CPU oracle sample (0: all rows)")
     ap.add_argument("--profile-run", action="store_true")
@@ -184,7 +189,7 @@ def summarize_trace(trace_dir: str, out: str):
         "# rocprofv3 kernel-trace stats of a bench run (dense-up W4 g32, M = 1, 4, 16)",
         "# commands (from the repository root on the GPU host):",
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d <D> -o run -- "
-        "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+        "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-layer",
         f"#   python3 bench.py --summarize-trace <D> {out}",
         "# name | calls | average_us | min_us | max_us | total_percent",
     ]
@@ -254,6 +259,59 @@ def cpu_baseline(p, shape, rows: int, min_seconds: float = 10.0):
                    f"each pass one call at each of M={list(CELLS_M)}; fp64 dequantize-then-dot; "
                    f"{dt:.1f} s"),
     }
+
+
+def measure_layer(qmm, dev, stream, capture):
+    """One decoder layer of the layer sweep (q, k, v, o, gate, up, down; 4-bit
+    G=32) at each sweep M: the seven projections one launch each, and with
+    q/k/v and gate/up fused (qmm_forward_fused: four launches). Weight copies
+    rotate over more than 512 MB as in the headline cells; graph replay."""
+    shapes = [(name, W.Shape(f"L0.{name}", K=K, N=N, bits=4, G=32), j)
+              for j, (name, K, N) in enumerate(W.LAYER_PROJECTIONS)]
+    layer_bytes = sum(sh.weight_bytes for _, sh, _ in shapes)
+    base = {}
+    for name, sh, seed in shapes:
+        pr = qmm_inputs.make_problem(seed=seed, M=max(W.SWEEP_M), K=sh.K, N=sh.N, bits=4, G=32,
+                                     packed_words=True)
+        base[name] = (torch.from_numpy(pr.words.view(np.int32)).to(dev),
+                      torch.from_numpy(pr.scales).to(dev), torch.from_numpy(pr.biases).to(dev),
+                      torch.from_numpy(pr.x).to(dev))
+    copies = max(2, -(-ROTATION_BYTES // layer_bytes))
+    sets = [{n: t[:3] for n, t in base.items()}]
+    sets += [{n: tuple(u.clone() for u in t[:3]) for n, t in base.items()} for _ in range(copies - 1)]
+    out = {"workload": (f"one dense decoder layer of the sweep ({', '.join(n for n, _, _ in shapes)}; "
+                        f"4-bit G=32), {layer_bytes / 1e6:.2f} MB of weights"),
+           "weight_copies_rotated": copies}
+    for M in W.SWEEP_M:
+        xs = {n: t[3][:M].contiguous() for n, t in base.items()}
+        ys = {n: torch.empty((M, sh.N), dtype=torch.float32, device=dev) for n, sh, _ in shapes}
+
+        def separate(i):
+            st = sets[i % copies]
+            for n, _, _ in shapes:
+                qmm.qmm_forward(xs[n], *st[n], 4, 32, out=ys[n])
+
+        def fused(i):
+            st = sets[i % copies]
+            qmm.qmm_forward_fused(xs["q"], [st["q"], st["k"], st["v"]], 4, 32,
+                                  outs=[ys["q"], ys["k"], ys["v"]])
+            qmm.qmm_forward(xs["o"], *st["o"], 4, 32, out=ys["o"])
+            qmm.qmm_forward_fused(xs["gate"], [st["gate"], st["up"]], 4, 32,
+                                  outs=[ys["gate"], ys["up"]])
+            qmm.qmm_forward(xs["down"], *st["down"], 4, 32, out=ys["down"])
+
+        cell = {}
+        reps = 4 * copies
+        for label, fn in (("separate", separate), ("fused", fused)):
+            g = capture(fn, reps)
+            g.replay()
+            torch.cuda.synchronize()
+            ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
+            del g
+            cell[f"{label}_us"] = round(ms * 1e3, 2)
+            cell[f"{label}_weight_GBps"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+        out[f"M{M}"] = cell
+    return out
 
 
 PROFILE_REPS = 4
@@ -397,6 +455,8 @@ def main():
             "traffic": None if traffic is None else round(traffic),
         },
     }
+    if not args.no_layer:
+        out["layer"] = measure_layer(qmm, dev, stream, capture)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, shape, args.cpu_rows)
     print(json.dumps(out), flush=True)

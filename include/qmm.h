@@ -134,6 +134,32 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
                          const uint16_t *biases, float *y, int M, int K, int N, int bits,
                          int G, hipStream_t stream);
 
+/*
+ * qmm_forward_fused - several projections of the same activations in one
+ * launch: y_p = x . W_p^T for p < count (count <= QMM_MAX_FUSED).
+ *
+ * The DS4Server QWEN38 performance page runs the gate and up projections of
+ * a layer as one merged projection ("MTPLX logic review") and promotes the
+ * exact fused projection ("A/B evidence" table); fusing q/k/v or gate/up
+ * also fills the GPU when a single projection has few output rows.
+ *
+ * x          [M, K] fp16, shared by every projection.
+ * wq, scales, biases, y, N: host arrays of `count` entries; entry p holds
+ *            the device pointers and the output-row count of projection p,
+ *            with the layouts and alignment of qmm_forward (y[p] is
+ *            [M, N[p]] fp32, overwritten).
+ * M, K, bits, G are common to all projections. The kernel is the one
+ * qmm_forward picks for (M, K, bits, G); each y[p] is bitwise equal to the
+ * qmm_forward result for projection p alone. Errors: those of qmm_forward for
+ * any projection, QMM_ERR_NULL for a NULL array, QMM_ERR_SHAPE for count out
+ * of range. The host arrays are read during the call only. Async on `stream`.
+ */
+#define QMM_MAX_FUSED 4
+int qmm_forward_fused(const uint16_t *x, int count, const uint32_t *const *wq,
+                      const uint16_t *const *scales, const uint16_t *const *biases,
+                      float *const *y, const int *N, int M, int K, int bits, int G,
+                      hipStream_t stream);
+
 /* Bytes of workspace qmm_forward_splitk needs: split_k * M * N * 4 for
  * split_k >= 2, 0 for split_k == 1 and for invalid arguments. */
 size_t qmm_splitk_workspace_bytes(int M, int N, int split_k);

@@ -91,3 +91,23 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 6, 64) == "mfma"
+
+
+def test_fused_rejects_before_launch():
+    """qmm_forward_fused checks its arrays and every projection on the host."""
+    lib = qmm._lib
+    good = (ctypes.c_void_p * 2)(4096, 8192)
+    ns = (ctypes.c_int * 2)(16, 8)
+    assert lib.qmm_forward_fused(4096, 2, None, good, good, good, ns, 1, 64, 4, 32, None) == -1
+    assert lib.qmm_forward_fused(None, 2, good, good, good, good, ns, 1, 64, 4, 32, None) == -1
+    assert lib.qmm_forward_fused(4096, 0, good, good, good, good, ns, 1, 64, 4, 32, None) == -2
+    assert lib.qmm_forward_fused(4096, qmm.QMM_MAX_FUSED + 1, good, good, good, good, ns, 1, 64,
+                                 4, 32, None) == -2
+    assert lib.qmm_forward_fused(4096, 2, good, good, good, good, ns, 1, 64, 3, 32, None) == -3
+    assert lib.qmm_forward_fused(4096, 2, good, good, good, good, ns, 1, 64, 4, 48, None) == -4
+    bad_n = (ctypes.c_int * 2)(16, 0)
+    assert lib.qmm_forward_fused(4096, 2, good, good, good, good, bad_n, 1, 64, 4, 32, None) == -2
+    odd = (ctypes.c_void_p * 2)(4096, 8200)  # second projection's pointer misaligned
+    assert lib.qmm_forward_fused(4096, 2, odd, good, good, good, ns, 1, 64, 4, 32, None) == -7
+    null_p = (ctypes.c_void_p * 2)(4096, None)
+    assert lib.qmm_forward_fused(4096, 2, good, good, null_p, good, ns, 1, 64, 4, 32, None) == -1
