@@ -3,8 +3,8 @@
 Every ``csrc/*.hip`` file is compiled with hipcc for gfx950 only and linked
 into one shared library exporting the C ABI of ``include/qmm.h``.
 
-The build also compiles each file's device code to assembly and fails if any
-kernel spills registers to scratch memory: the kernels are designed to fit
+The build also reads the compiler's kernel-resource-usage remarks and fails if
+any kernel spills registers to scratch memory: the kernels are designed to fit
 their registers, and spilled variants of the matrix-core kernels have produced
 wrong results with this toolchain.
 """
@@ -37,34 +37,45 @@ FLAGS = [
 def _run(cmd, src: Path):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    text = res.stdout + res.stderr
     if res.returncode != 0:
+        err = "\n".join(l for l in text.splitlines() if noise not in l and "remark:" not in l)
         raise RuntimeError(f"hipcc failed for {src.name}:\n{err}")
-    return err
+    return text
 
 
-def _check_no_scratch(asm: Path, src: Path):
-    """Fail if a kernel in the device assembly uses scratch (register spills)."""
-    text = asm.read_text()
-    bad = []
-    for block in text.split("  - .agpr_count:")[1:]:
-        name = re.search(r"\.name:\s+(\S+)", block)
-        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
-        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
-        if name and ((priv and int(priv.group(1))) or (spill and int(spill.group(1)))):
-            bad.append(name.group(1))
+def _check_no_scratch(text: str, src: Path):
+    """Fail if a kernel uses scratch (register spills), from the compiler's
+    kernel-resource-usage remarks."""
+    bad, name = [], None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) and name not in bad:
+            bad.append(name)
     if bad:
         raise RuntimeError(f"{src.name}: kernels spill to scratch memory: {bad[:4]}")
 
 
 def _compile(src: Path) -> Path:
     obj = BUILD_DIR / (src.stem + ".o")
-    asm = BUILD_DIR / (src.stem + ".s")
-    err = _run([HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)], src)
-    _run([HIPCC, *FLAGS, "--cuda-device-only", "-S", str(src), "-o", str(asm)], src)
-    _check_no_scratch(asm, src)
-    if err.strip():
-        print(err, file=sys.stderr)
+    text = _run([HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", str(src), "-o", str(obj)], src)
+    _check_no_scratch(text, src)
+    lines, skip = [], 0
+    for l in text.splitlines():  # warnings only: drop the remarks and the feature notice
+        if "remark:" in l:
+            skip = 2  # the source line and caret that follow a remark
+            continue
+        if skip:
+            skip -= 1
+            continue
+        if "is not a recognized feature for this target" not in l:
+            lines.append(l)
+    if "\n".join(lines).strip():
+        print("\n".join(lines), file=sys.stderr)
     return obj
 
 

@@ -15,7 +15,7 @@ static_assert(QMM_MAX_FUSED <= qmm::kMaxProj, "the launch arguments hold every f
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool bits_supported(int bits) { return bits == 4 || bits == 5 || bits == 6 || bits == 8; }
+bool bits_supported(int bits) { return bits >= 2 && bits <= 8 && bits != 7; }
 bool group_supported(int G) { return G == 32 || G == 64 || G == 128; }
 
 // Shape checks shared by every product entry point.
@@ -68,19 +68,24 @@ bool xr_supported(int K, int N, int bits, int G, int split)
 
 // One and two rows: the row-exact VALU kernel (measured on the 5120 x 17408
 // 4-bit projection: 12.8 and 17.9 us against 21.9 us for the matrix-core
-// kernel at two rows; from three rows on the matrix cores win).
+// kernel at two rows; from three rows on the matrix cores win). A shape that
+// neither matrix-core kernel takes (3-bit codes at G = 32 with K past the
+// register-resident kernel) runs on the VALU kernel, 8 rows per launch.
 Kernel choose_kernel(int M, int K, int N, int bits, int G, int split)
 {
     if (M <= kQmvMaxRows)
         return Kernel::qmv;
-    return xr_supported(K, N, bits, G, split) ? Kernel::mfma : Kernel::mfma_lds;
+    if (xr_supported(K, N, bits, G, split))
+        return Kernel::mfma;
+    return qmm::mfma_supported(bits, G) ? Kernel::mfma_lds : Kernel::qmv;
 }
 
 // Launch one product (all of M, in 16-row steps for the multi-row kernels)
 // writing either y (split == 1) or the split partials (y = workspace).
 int launch_args(Kernel kind, const qmm::ProductArgs &full, int bits, int G, hipStream_t stream)
 {
-    if (kind == Kernel::mfma && !xr_supported(full.K, full.N, bits, G, full.split))
+    if ((kind == Kernel::mfma && !xr_supported(full.K, full.N, bits, G, full.split)) ||
+        (kind == Kernel::mfma_lds && !qmm::mfma_supported(bits, G)))
         return QMM_ERR_UNSUPPORTED;
     const int M = full.M;
     const int step = kind == Kernel::qmv ? kQmvRowsPerLaunch : kMaxRowsPerLaunch;
@@ -115,7 +120,7 @@ const char *qmm_strerror(int code)
     case QMM_OK: return "success";
     case QMM_ERR_NULL: return "a required pointer is NULL";
     case QMM_ERR_SHAPE: return "bad shape: need M, K, N >= 1, K a multiple of G, sizes in range";
-    case QMM_ERR_BITS: return "unsupported bit width (supported: 4, 5, 6, 8)";
+    case QMM_ERR_BITS: return "unsupported bit width (supported: 2, 3, 4, 5, 6, 8)";
     case QMM_ERR_GROUP: return "unsupported group size (supported: 32, 64, 128)";
     case QMM_ERR_SPLIT: return "bad split_k: need 1 <= split_k <= K/G";
     case QMM_ERR_WORKSPACE: return "workspace smaller than qmm_splitk_workspace_bytes(M, N, split_k)";

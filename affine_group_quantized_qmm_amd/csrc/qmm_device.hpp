@@ -44,12 +44,13 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 // Codes are paired (i, i+d) inside blocks of 2d consecutive codes, with d
 // chosen per width so that code i+d always lands in the upper half of a
 // window whose lower half holds code i:
+//   bits 2: d = 4 ( 8 bits apart)   bits 3: d = 4 (12 bits apart)
 //   bits 4: d = 4 (16 bits apart)   bits 5: d = 4 (20 bits apart)
 //   bits 6: d = 2 (12 bits apart)   bits 8: d = 2 (16 bits apart)
 // Pair P of a run of codes therefore holds codes lo(P) and lo(P) + d, and
 // the activations are stored in the same pair order ("permuted order").
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr int pair_dist(int bits) { return (bits == 4 || bits == 5) ? 4 : 2; }
+__host__ __device__ constexpr int pair_dist(int bits) { return bits <= 5 ? 4 : 2; }
 
 // Index (within a run of codes starting at a block boundary) of the lower
 // code of pair P, and of the code at permuted position `pos`.
@@ -178,7 +179,7 @@ __device__ __forceinline__ void unpack_pairs_impl(const uint32_t (&w)[NW], half2
 }
 
 // Widen NCODES codes (stored from bit 0 of w) into NCODES/2 fp16 pairs in
-// pair order: exact integers for 5, 6 and 8 bits, 64 + code for 4 bits.
+// pair order: exact integers for 2, 3, 5, 6 and 8 bits, 64 + code for 4 bits.
 template <int BITS, int NCODES, int NW>
 __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&out)[NCODES / 2])
 {

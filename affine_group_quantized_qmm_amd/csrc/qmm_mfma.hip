@@ -385,10 +385,29 @@ hipError_t launch_mfma_t(const ProductArgs &a, hipStream_t stream)
 
 }  // namespace
 
+// Every (bits, G) whose lane chunks can be loaded without reading past their
+// group; 3-bit codes at G = 32 cannot (a 24-bit chunk straddles words and
+// the last lane block would need the next group's word).
+bool mfma_supported(int bits, int G)
+{
+#define QMM_MFMA_FITS(B, GG) \
+    if (bits == B && G == GG) return Geometry<B, GG>::fits();
+    QMM_MFMA_FITS(2, 32) QMM_MFMA_FITS(2, 64) QMM_MFMA_FITS(2, 128)
+    QMM_MFMA_FITS(3, 32) QMM_MFMA_FITS(3, 64) QMM_MFMA_FITS(3, 128)
+    QMM_MFMA_FITS(4, 32) QMM_MFMA_FITS(4, 64) QMM_MFMA_FITS(4, 128)
+    QMM_MFMA_FITS(5, 32) QMM_MFMA_FITS(5, 64) QMM_MFMA_FITS(5, 128)
+    QMM_MFMA_FITS(6, 32) QMM_MFMA_FITS(6, 64) QMM_MFMA_FITS(6, 128)
+    QMM_MFMA_FITS(8, 32) QMM_MFMA_FITS(8, 64) QMM_MFMA_FITS(8, 128)
+#undef QMM_MFMA_FITS
+    return false;
+}
+
 hipError_t launch_mfma(const ProductArgs &a, int bits, int G, hipStream_t stream)
 {
 #define QMM_MFMA_CASE(B, GG) \
     if (bits == B && G == GG) return launch_mfma_t<B, GG>(a, stream);
+    QMM_MFMA_CASE(2, 32) QMM_MFMA_CASE(2, 64) QMM_MFMA_CASE(2, 128)
+    QMM_MFMA_CASE(3, 64) QMM_MFMA_CASE(3, 128)
     QMM_MFMA_CASE(4, 32) QMM_MFMA_CASE(4, 64) QMM_MFMA_CASE(4, 128)
     QMM_MFMA_CASE(5, 32) QMM_MFMA_CASE(5, 64) QMM_MFMA_CASE(5, 128)
     QMM_MFMA_CASE(6, 32) QMM_MFMA_CASE(6, 64) QMM_MFMA_CASE(6, 128)

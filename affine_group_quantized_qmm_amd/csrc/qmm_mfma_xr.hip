@@ -45,7 +45,7 @@ constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after 
 // variant of a width whose parts fit the workgroup (xr_variants).
 constexpr int xr_stages(int bits, int xc)
 {
-    return bits == 4 ? (xc <= 640 ? 3 : 2) : bits == 8 ? 2 : (xc <= 640 ? 2 : 1);
+    return bits <= 4 ? (xc <= 640 ? 3 : 2) : bits == 8 ? 2 : (xc <= 640 ? 2 : 1);
 }
 // Two-byte scale/bias loads (odd group counts) take twice the load registers:
 // one stage fewer, so that no variant spills.
@@ -98,12 +98,16 @@ __device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int g
 }
 
 // Dynamic LDS of one workgroup of KP waves: per wave a weight tile region
-// (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), then two
+// (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), at least as
+// large as the group-sum scratch of the start (XG x 64 floats), then two
 // buffers of kXrBatch tiles of partial sums.
 template <int BITS, int G, int XC>
 __host__ __device__ constexpr size_t xr_wave_lds()
 {
-    return 16 * (size_t)XrGeo<BITS, G, XC>::LSTR + 16 * 4 * (size_t)XrGeo<BITS, G, XC>::SBSTR;
+    using Geo = XrGeo<BITS, G, XC>;
+    const size_t run = 16 * (size_t)Geo::LSTR + 16 * 4 * (size_t)Geo::SBSTR;
+    const size_t xs = (size_t)Geo::XG * 4 * 16 * sizeof(float);
+    return run > xs ? run : xs;
 }
 template <int BITS, int G, int XC>
 __host__ __device__ constexpr size_t xr_lds_bytes(int KP)
@@ -253,8 +257,8 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     // Group sums XS[row i][group 4u + c] of this part, as the A operand of
     // one fp32 MFMA per group quad (the bias term sum_g b'[n][g] XS[m][g]).
     // Lane block c sums its quarter of every group with v_dot2 against
-    // (1, 1); the quarters meet in the (still unused) weight LDS region and
-    // are added in lane-block order.
+    // (1, 1); the quarters meet in the wave's (still unused) LDS region,
+    // sized for them, and are added in lane-block order.
     float xsa[Geo::XQ];
     {
         float *xsl = reinterpret_cast<float *>(wmy);
@@ -528,6 +532,8 @@ bool mfma_xr_supported(const ProductArgs &a, int bits, int G)
     int xc;
 #define QMM_XR_CASE(B, GG) \
     if (bits == B && G == GG) return plan_xr_any<B, GG>(a, plan, xc);
+    QMM_XR_CASE(2, 32) QMM_XR_CASE(2, 64) QMM_XR_CASE(2, 128)
+    QMM_XR_CASE(3, 32) QMM_XR_CASE(3, 64) QMM_XR_CASE(3, 128)
     QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)
     QMM_XR_CASE(5, 32) QMM_XR_CASE(5, 64) QMM_XR_CASE(5, 128)
     QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)
@@ -542,6 +548,8 @@ hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t str
     hipError_t e = hipErrorInvalidValue;
 #define QMM_XR_CASE(B, GG) \
     if (bits == B && G == GG) e = launch_xr_t<B, GG>(a, stream, done);
+    QMM_XR_CASE(2, 32) QMM_XR_CASE(2, 64) QMM_XR_CASE(2, 128)
+    QMM_XR_CASE(3, 32) QMM_XR_CASE(3, 64) QMM_XR_CASE(3, 128)
     QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)
     QMM_XR_CASE(5, 32) QMM_XR_CASE(5, 64) QMM_XR_CASE(5, 128)
     QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)

@@ -60,6 +60,8 @@ hipError_t launch_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int
     const size_t total = (size_t)N * K * bits / 32;
     const dim3 grid(grid_for(total, 256)), block(256);
     switch (bits) {
+    case 2: hipLaunchKernelGGL(pack_kernel<2>, grid, block, 0, stream, codes, packed, N, K); break;
+    case 3: hipLaunchKernelGGL(pack_kernel<3>, grid, block, 0, stream, codes, packed, N, K); break;
     case 4: hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, stream, codes, packed, N, K); break;
     case 5: hipLaunchKernelGGL(pack_kernel<5>, grid, block, 0, stream, codes, packed, N, K); break;
     case 6: hipLaunchKernelGGL(pack_kernel<6>, grid, block, 0, stream, codes, packed, N, K); break;

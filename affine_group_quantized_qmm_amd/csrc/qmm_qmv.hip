@@ -364,6 +364,8 @@ hipError_t launch_qmv(const ProductArgs &a, int bits, int G, hipStream_t stream)
 {
 #define QMM_QMV_CASE(B, GG) \
     if (bits == B && G == GG) return launch_qmv_t<B, GG>(a, stream);
+    QMM_QMV_CASE(2, 32) QMM_QMV_CASE(2, 64) QMM_QMV_CASE(2, 128)
+    QMM_QMV_CASE(3, 32) QMM_QMV_CASE(3, 64) QMM_QMV_CASE(3, 128)
     QMM_QMV_CASE(4, 32) QMM_QMV_CASE(4, 64) QMM_QMV_CASE(4, 128)
     QMM_QMV_CASE(5, 32) QMM_QMV_CASE(5, 64) QMM_QMV_CASE(5, 128)
     QMM_QMV_CASE(6, 32) QMM_QMV_CASE(6, 64) QMM_QMV_CASE(6, 128)

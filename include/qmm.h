@@ -29,9 +29,10 @@
  *   biases  fp16 [N, K/G]
  *   y       fp32 [M, N]            overwritten, never accumulated into
  *
- * Supported: bits in {4, 5, 6, 8} (the formats consumed as stored in the
- * "Qwen3.8 Flash Next performance and parity receipt" page, section
- * "MTPLX logic review", plus the 5/6-bit widths of the "LaneQMM" commit);
+ * Supported: bits in {2, 3, 4, 5, 6, 8} (the 2/4/8-bit formats consumed as
+ * stored in the "Qwen3.8 Flash Next performance and parity receipt" page,
+ * section "MTPLX logic review", the 5/6-bit widths of the "LaneQMM" commit of
+ * the vmlx-swift pull request #565 page, and 3 bits between them);
  * G in {32, 64, 128}; K a positive multiple of G; N >= 1; M >= 1 (tuned for
  * M = 1..16 verify rows; larger M is processed 16 rows at a time).
  *
@@ -62,7 +63,7 @@ extern "C" {
 #define QMM_OK 0
 #define QMM_ERR_NULL (-1)          /* a required pointer is NULL */
 #define QMM_ERR_SHAPE (-2)         /* M < 1, K < 1, N < 1, K % G != 0 or a size overflows */
-#define QMM_ERR_BITS (-3)          /* bits not in {4, 5, 6, 8} */
+#define QMM_ERR_BITS (-3)          /* bits not in {2, 3, 4, 5, 6, 8} */
 #define QMM_ERR_GROUP (-4)         /* G not in {32, 64, 128} */
 #define QMM_ERR_SPLIT (-5)         /* split_k < 1 or split_k > K/G */
 #define QMM_ERR_WORKSPACE (-6)     /* workspace smaller than qmm_splitk_workspace_bytes */
@@ -138,9 +139,9 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
  * qmm_forward_fused - several projections of the same activations in one
  * launch: y_p = x . W_p^T for p < count (count <= QMM_MAX_FUSED).
  *
- * The DS4Server QWEN38 performance page runs the gate and up projections of
- * a layer as one merged projection ("MTPLX logic review") and promotes the
- * exact fused projection ("A/B evidence" table); fusing q/k/v or gate/up
+ * The "Qwen3.8 Flash Next performance and parity receipt" page runs the gate
+ * and up projections of a layer as one merged projection (section "MTPLX
+ * logic review") and promotes the exact fused projection ("A/B evidence"); fusing q/k/v or gate/up
  * also fills the GPU when a single projection has few output rows.
  *
  * x          [M, K] fp16, shared by every projection.
@@ -189,8 +190,9 @@ const char *qmm_kernel_name(int M, int K, int N, int bits, int G);
  *              short enough for 8 parts of 768 activations, 512 for 8-bit
  *              codes); QMM_ERR_UNSUPPORTED otherwise;
  *   "mfma_lds" the multi-row matrix-core kernel that streams activations
- *              through LDS; any shape; qmm_forward's choice for M >= 3 when
- *              "mfma" does not apply.
+ *              through LDS; any shape except 3-bit codes at G = 32
+ *              (QMM_ERR_UNSUPPORTED); qmm_forward's choice for M >= 3 when
+ *              "mfma" does not apply (and "qmv" when neither does).
  * Same arguments, layout and errors as qmm_forward; an unknown name returns
  * QMM_ERR_SHAPE, a NULL name QMM_ERR_NULL. */
 int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,

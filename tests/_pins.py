@@ -90,7 +90,7 @@ def pack_golden(o) -> list[str]:
 
 def single_code(o) -> list[str]:
     fails = []
-    for bits in (4, 5, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         K = 64  # two groups of 32
         values = np.arange(1, 1 << bits, dtype=np.uint32)
         rows = []
@@ -119,7 +119,7 @@ def single_code(o) -> list[str]:
 def round_trip(o) -> list[str]:
     fails = []
     rng = np.random.default_rng(1234)
-    for bits in (4, 5, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         for K in (32, 64, 96, 512):
             Q = rng.integers(0, 1 << bits, size=(7, K), dtype=np.uint8)
             W = o.pack(Q, bits)
@@ -178,7 +178,7 @@ def forward_golden(o) -> list[str]:
 def integer_matmul(o) -> list[str]:
     fails = []
     rng = np.random.default_rng(99)
-    for bits in (4, 5, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         for G in (32, 64):
             M, K, N = 3, 128, 37
             Q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
@@ -240,7 +240,7 @@ def _random_problem(rng, M, K, N, bits, G):
 def one_hot(o) -> list[str]:
     fails = []
     rng = np.random.default_rng(7)
-    for bits, G in ((4, 32), (5, 64), (6, 32), (8, 64)):
+    for bits, G in ((2, 32), (3, 64), (4, 32), (5, 64), (6, 32), (8, 64)):
         K, N = 128, 19
         Q, words, s, b, _ = _random_problem(rng, 1, K, N, bits, G)
         x = np.zeros((K, K), dtype=np.float16)
@@ -256,7 +256,7 @@ def one_hot(o) -> list[str]:
 def ones(o) -> list[str]:
     fails = []
     rng = np.random.default_rng(8)
-    for bits, G in ((4, 32), (5, 32), (6, 64), (8, 32)):
+    for bits, G in ((2, 64), (3, 32), (4, 32), (5, 32), (6, 64), (8, 32)):
         K, N = 256, 23
         Q, words, s, b, _ = _random_problem(rng, 1, K, N, bits, G)
         x = np.ones((1, K), dtype=np.float16)

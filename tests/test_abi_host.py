@@ -51,7 +51,7 @@ def v(**kw):
 
 def test_validation_accepts_good_arguments():
     assert v() == 0
-    for bits in (4, 5, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         for G in (32, 64, 128):
             assert v(bits=bits, G=G, K=G * 3) == 0
     need = qmm.qmm_splitk_workspace_bytes(4, 256, 3)
@@ -66,7 +66,7 @@ def test_validation_accepts_good_arguments():
     (dict(split=2, ws=0, wsb=1 << 20), -1),
     (dict(M=0), -2), (dict(K=0), -2), (dict(N=0), -2), (dict(K=100), -2), (dict(K=48, G=32), -2),
     (dict(N=-5), -2), (dict(K=1 << 29), -2),
-    (dict(bits=3), -3), (dict(bits=7), -3), (dict(bits=16), -3),
+    (dict(bits=1), -3), (dict(bits=7), -3), (dict(bits=16), -3),
     (dict(G=16), -4), (dict(G=96), -4),
     (dict(split=-1, ws=A, wsb=1 << 30), -5), (dict(split=17, ws=A, wsb=1 << 30), -5),
     (dict(split=2, ws=A, wsb=100), -6),
@@ -82,7 +82,7 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(2, 5120, 17408, 4, 32) == "qmv"
     assert qmm.qmm_kernel_name(3, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 4, 32) == "mfma"
-    assert qmm.qmm_kernel_name(16, 5120, 17408, 3, 32) is None
+    assert qmm.qmm_kernel_name(16, 5120, 17408, 7, 32) is None
     # activations of K = 17408 do not fit 8 parts of 768: the LDS-streaming kernel
     assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 6144, 1024, 4, 32) == "mfma"
@@ -91,6 +91,14 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 6, 64) == "mfma"
+    # 2- and 3-bit codes
+    assert qmm.qmm_kernel_name(2, 5120, 1000, 2, 32) == "qmv"
+    assert qmm.qmm_kernel_name(8, 5120, 1000, 2, 32) == "mfma"
+    assert qmm.qmm_kernel_name(8, 5120, 1000, 3, 32) == "mfma"
+    # past the register-resident kernel: LDS kernel, except 3-bit G=32 (VALU kernel)
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 2, 32) == "mfma_lds"
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 64) == "mfma_lds"
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 32) == "qmv"
 
 
 def test_fused_rejects_before_launch():
@@ -103,7 +111,7 @@ def test_fused_rejects_before_launch():
     assert lib.qmm_forward_fused(4096, 0, good, good, good, good, ns, 1, 64, 4, 32, None) == -2
     assert lib.qmm_forward_fused(4096, qmm.QMM_MAX_FUSED + 1, good, good, good, good, ns, 1, 64,
                                  4, 32, None) == -2
-    assert lib.qmm_forward_fused(4096, 2, good, good, good, good, ns, 1, 64, 3, 32, None) == -3
+    assert lib.qmm_forward_fused(4096, 2, good, good, good, good, ns, 1, 64, 7, 32, None) == -3
     assert lib.qmm_forward_fused(4096, 2, good, good, good, good, ns, 1, 64, 4, 48, None) == -4
     bad_n = (ctypes.c_int * 2)(16, 0)
     assert lib.qmm_forward_fused(4096, 2, good, good, good, good, bad_n, 1, 64, 4, 32, None) == -2

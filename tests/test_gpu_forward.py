@@ -10,7 +10,7 @@ from tests import _gpu
 
 pytestmark = pytest.mark.gpu
 
-BITS_G = [(b, g) for b in (4, 5, 6, 8) for g in (32, 64, 128)]
+BITS_G = [(b, g) for b in (2, 3, 4, 5, 6, 8) for g in (32, 64, 128)]
 
 
 @pytest.mark.parametrize("bits,G", BITS_G)
@@ -30,26 +30,31 @@ KERNELS = ["qmv", "mfma", "mfma_lds"]
 
 
 def run_kernel(kernel, dp, bits, G):
-    """Forced-kernel call; "mfma" on a shape it cannot run must say so, and
-    then qmm_forward must not pick it."""
+    """Forced-kernel call; "mfma" on a shape it cannot run (and "mfma_lds" on
+    3-bit codes at G = 32) must say so, and then qmm_forward must not pick it."""
     qmm = _gpu.lib()
     try:
         return qmm.qmm_forward_kernel(kernel, dp.x, dp.wq, dp.s, dp.b, bits, G)
     except qmm.QmmError as e:
-        assert kernel == "mfma" and e.code == qmm.QMM_ERR_UNSUPPORTED, str(e)
+        assert e.code == qmm.QMM_ERR_UNSUPPORTED, str(e)
+        assert kernel == "mfma" or (kernel == "mfma_lds" and (bits, G) == (3, 32)), str(e)
         M, K, N = dp.p.M, dp.p.K, dp.p.N
-        assert qmm.qmm_kernel_name(max(M, 3), K, N, bits, G) == "mfma_lds"
+        assert qmm.qmm_kernel_name(max(M, 3), K, N, bits, G) != kernel
         return None
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("bits,G,K", [(4, 32, 1280), (5, 64, 2560), (6, 32, 1280), (8, 128, 2048),
-                                      (8, 64, 4096)])
+                                      (8, 64, 4096), (2, 32, 1280), (2, 128, 4096), (3, 32, 1280),
+                                      (3, 64, 2560)])
 def test_each_kernel(kernel, M, bits, G, K):
     N = 97
     dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=11, M=M, K=K, N=N, bits=bits, G=G))
     y = run_kernel(kernel, dp, bits, G)
+    if (kernel, bits, G) == ("mfma_lds", 3, 32):
+        assert y is None
+        return
     assert y is not None, f"{kernel} should support bits={bits} G={G} K={K}"
     torch.cuda.synchronize()
     ref, absum = dp.oracle()

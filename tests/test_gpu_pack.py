@@ -9,7 +9,7 @@ from tests import _gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("bits", [4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (17, 96), (64, 512), (129, 1056), (5, 5120)])
 def test_pack_bit_exact(bits, N, K):
     qmm = _gpu.lib()
@@ -21,7 +21,7 @@ def test_pack_bit_exact(bits, N, K):
     assert np.array_equal(got, oracle.get().pack(codes, bits))
 
 
-@pytest.mark.parametrize("bits", [4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_pack_ignores_high_bits(bits):
     """Bits above `bits` in an input byte are not stored."""
     qmm = _gpu.lib()

@@ -34,6 +34,6 @@ def test_rowexact_rejects_like_forward():
     y = torch.empty((2, 8), dtype=torch.float32, device=dp.x.device)
     ptrs = (dp.x.data_ptr(), dp.wq.data_ptr(), dp.s.data_ptr(), dp.b.data_ptr(), y.data_ptr())
     stream = torch.cuda.current_stream().cuda_stream
-    for bits, G, code in ((3, 32, -3), (4, 48, -4)):
+    for bits, G, code in ((7, 32, -3), (4, 48, -4)):
         assert qmm._lib.qmm_forward_rowexact(*ptrs, 2, 64, 8, bits, G, stream) == code
         assert qmm._lib.qmm_forward(*ptrs, 2, 64, 8, bits, G, stream) == code
