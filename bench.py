@@ -15,7 +15,9 @@ call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 Prints one JSON line. Synthetic data (seeded; no trained weights). Besides
 the headline cells the line carries `layer`: one decoder layer of the layer
 sweep at M = 1 and 8, its seven projections launched one by one and with
-q/k/v and gate/up fused (qmm_forward_fused).
+q/k/v and gate/up fused (qmm_forward_fused); and `other_workloads`: the
+dense up projection with 2- and 3-bit codes and the mixed 5/6/8-bit G=64
+projections, timed like the headline cells.
 
 The roofline object covers the kernel that takes most of a step. Its
 `traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE and
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
-                    help="skip the decoder-layer cell (separate vs fused projections)")
+                    help="skip the decoder-layer cell and the other workloads")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="output rows of the CPU oracle sample (0: all rows)")
     ap.add_argument("--profile-run", action="store_true")
@@ -259,6 +261,48 @@ def cpu_baseline(p, shape, rows: int, min_seconds: float = 10.0):
                    f"each pass one call at each of M={list(CELLS_M)}; fp64 dequantize-then-dot; "
                    f"{dt:.1f} s"),
     }
+
+
+# Other workloads, timed like the headline cells (not part of `value`):
+# the dense up projection with 2- and 3-bit codes, and the mixed 5/6/8-bit
+# G=64 projections.
+EXTRA_SHAPES = ((W.Shape("dense_up_5120x17408_w2g32", K=5120, N=17408, bits=2, G=32), (1, 16)),
+                (W.Shape("dense_up_5120x17408_w3g32", K=5120, N=17408, bits=3, G=32), (1, 16)),
+                *((sh, W.MIXED_M) for sh in W.MIXED))
+
+
+def measure_cells(qmm, shape, Ms, dev, stream, capture):
+    """Per-M launch times of qmm_forward on `shape` (rotated weight copies, graph replay)."""
+    p = qmm_inputs.make_problem(seed=5, M=max(Ms), K=shape.K, N=shape.N, bits=shape.bits,
+                                G=shape.G, packed_words=True)
+    wq = torch.from_numpy(p.words.view(np.int32)).to(dev)
+    s = torch.from_numpy(p.scales).to(dev)
+    b = torch.from_numpy(p.biases).to(dev)
+    copies = max(2, -(-ROTATION_BYTES // shape.weight_bytes))
+    sets = [(wq, s, b)] + [(wq.clone(), s.clone(), b.clone()) for _ in range(copies - 1)]
+    x = torch.from_numpy(p.x).to(dev)
+    out = {"K": shape.K, "N": shape.N, "bits": shape.bits, "G": shape.G,
+           "weight_bytes_per_call": shape.weight_bytes, "weight_copies_rotated": copies}
+    for M in Ms:
+        xm = x[:M].contiguous()
+        y = torch.empty((M, shape.N), dtype=torch.float32, device=dev)
+
+        def call(i, xm=xm, y=y):
+            qmm.qmm_forward(xm, *sets[i % copies], shape.bits, shape.G, out=y)
+
+        reps = max(50, 2 * copies)
+        g = capture(call, reps)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
+        del g
+        out[f"M{M}"] = {
+            "kernel": qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G),
+            "us_per_call": round(ms * 1e3, 3),
+            "weight_GBps": round(shape.weight_bytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * shape.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        }
+    return out
 
 
 def measure_layer(qmm, dev, stream, capture):
@@ -457,6 +501,8 @@ def main():
     }
     if not args.no_layer:
         out["layer"] = measure_layer(qmm, dev, stream, capture)
+        out["other_workloads"] = {sh.name: measure_cells(qmm, sh, Ms, dev, stream, capture)
+                                  for sh, Ms in EXTRA_SHAPES}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, shape, args.cpu_rows)
     print(json.dumps(out), flush=True)
