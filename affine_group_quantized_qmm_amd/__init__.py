@@ -36,6 +36,10 @@ _lib.qmm_forward_rowexact.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p
 _lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
 _lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_fused.argtypes = [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
+_lib.qmm_tiled_bytes.argtypes = [_i, _i, _i, _i, ctypes.POINTER(_sz)]
+_lib.qmm_tiled_bytes.restype = _sz
+_lib.qmm_repack_tiled.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
+_lib.qmm_forward_tiled.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.qmm_splitk_workspace_bytes.restype = _sz
 _lib.qmm_validate.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz]
@@ -44,12 +48,14 @@ _lib.qmm_strerror.restype = ctypes.c_char_p
 _lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
 _lib.qmm_kernel_name.restype = ctypes.c_char_p
 for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_splitk,
-           _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_validate):
+           _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_repack_tiled,
+           _lib.qmm_forward_tiled, _lib.qmm_validate):
     _f.restype = _i
 
 EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_splitk",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
-            "qmm_forward_kernel", "qmm_forward_fused")
+            "qmm_forward_kernel", "qmm_forward_fused", "qmm_tiled_bytes", "qmm_repack_tiled",
+            "qmm_forward_tiled")
 
 QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 
@@ -194,6 +200,51 @@ def qmm_forward_fused(x, projections, bits: int, G: int, outs=None) -> list[torc
     if rc:
         raise QmmError(rc, "qmm_forward_fused")
     return outs
+
+
+def qmm_tiled_bytes(N: int, K: int, bits: int, G: int) -> tuple[int, int]:
+    """(code bytes, (s, b) word bytes) of the tiled layout; (0, 0) if it does not exist."""
+    sb = _sz(0)
+    w = _lib.qmm_tiled_bytes(N, K, bits, G, ctypes.byref(sb))
+    return int(w), int(sb.value)
+
+
+def qmm_repack_tiled(wq, scales, biases, bits: int, G: int):
+    """The tiled (matrix-core) layout of packed weights: (uint8 codes, int32 (s, b) words)."""
+    N = wq.shape[0]
+    K = scales.shape[1] * G
+    _operands(torch.empty((1, K), dtype=torch.float16, device=wq.device), wq, scales, biases, bits, G)
+    wb, sbb = qmm_tiled_bytes(N, K, bits, G)
+    if not wb:
+        raise QmmError(QMM_ERR_UNSUPPORTED, "qmm_repack_tiled")
+    tw = torch.empty(wb, dtype=torch.uint8, device=wq.device)
+    tsb = torch.empty(sbb // 4, dtype=torch.int32, device=wq.device)
+    rc = _lib.qmm_repack_tiled(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), tw.data_ptr(),
+                               tsb.data_ptr(), N, K, bits, G, _stream(wq))
+    if rc:
+        raise QmmError(rc, "qmm_repack_tiled")
+    return tw, tsb
+
+
+def qmm_forward_tiled(x, tw, tsb, N: int, bits: int, G: int, out=None) -> torch.Tensor:
+    """y = x . W^T from the tiled layout (qmm_repack_tiled's output)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _check(x, "x", (torch.float16,), (M, K), None)
+    wb, sbb = qmm_tiled_bytes(N, K, bits, G)
+    if not wb:
+        raise QmmError(QMM_ERR_UNSUPPORTED, "qmm_forward_tiled")
+    _check(tw, "tiled_w", (torch.uint8,), (wb,), x.device)
+    _check(tsb, "tiled_sb", (torch.int32, torch.uint32), (sbb // 4,), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(out, "out", (torch.float32,), (M, N), x.device)
+    rc = _lib.qmm_forward_tiled(x.data_ptr(), tw.data_ptr(), tsb.data_ptr(), out.data_ptr(), M, K, N,
+                                bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_tiled")
+    return out
 
 
 def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,

@@ -252,6 +252,70 @@ int qmm_forward_fused(const uint16_t *x, int count, const uint32_t *const *wq,
     return launch_args(choose_kernel(M, K, a.N, bits, G, 1), a, bits, G, stream);
 }
 
+// Layouts the tiled form exists for (the repack); the product additionally
+// needs K parts that fit the kernel (qmm::tiled_supported).
+static bool tiled_layout_ok(int N, int K, int bits, int G)
+{
+    return (bits == 2 || bits == 4 || bits == 8) && group_supported(G) && N >= 1 && K >= G &&
+           K % (4 * G) == 0 && ((int64_t)K * bits) % 512 == 0 && (int64_t)K * bits < ((int64_t)1 << 31) &&
+           N < (1 << 30);
+}
+
+size_t qmm_tiled_bytes(int N, int K, int bits, int G, size_t *sb_bytes)
+{
+    if (sb_bytes)
+        *sb_bytes = 0;
+    if (!tiled_layout_ok(N, K, bits, G))
+        return 0;
+    const size_t rows = ((size_t)N + 15) / 16 * 16;
+    if (sb_bytes)
+        *sb_bytes = rows * (size_t)(K / G) * 4;
+    return rows * (size_t)K * bits / 8;
+}
+
+int qmm_repack_tiled(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases,
+                     uint8_t *tiled_w, uint32_t *tiled_sb, int N, int K, int bits, int G,
+                     hipStream_t stream)
+{
+    if (!wq || !scales || !biases || !tiled_w || !tiled_sb)
+        return QMM_ERR_NULL;
+    const int rc = check_shape(1, K, N, bits, G);
+    if (rc != QMM_OK)
+        return rc;
+    if (!tiled_layout_ok(N, K, bits, G))
+        return QMM_ERR_UNSUPPORTED;
+    if (!aligned16(wq) || !aligned16(scales) || !aligned16(biases) || !aligned16(tiled_w) ||
+        !aligned16(tiled_sb))
+        return QMM_ERR_ALIGN;
+    return qmm::launch_repack_tiled(wq, scales, biases, tiled_w, tiled_sb, N, K, bits, G, stream) ==
+                   hipSuccess
+               ? QMM_OK
+               : QMM_ERR_LAUNCH;
+}
+
+int qmm_forward_tiled(const uint16_t *x, const uint8_t *tiled_w, const uint32_t *tiled_sb, float *y,
+                      int M, int K, int N, int bits, int G, hipStream_t stream)
+{
+    if (!x || !tiled_w || !tiled_sb || !y)
+        return QMM_ERR_NULL;
+    const int rc = check_shape(M, K, N, bits, G);
+    if (rc != QMM_OK)
+        return rc;
+    if (!aligned16(x) || !aligned16(tiled_w) || !aligned16(tiled_sb) || !aligned16(y))
+        return QMM_ERR_ALIGN;
+    qmm::ProductArgs a = product_args(x, reinterpret_cast<const uint32_t *>(tiled_w),
+                                      reinterpret_cast<const uint16_t *>(tiled_sb), nullptr, y, M, K,
+                                      N, 1);
+    if (!tiled_layout_ok(N, K, bits, G) || !qmm::tiled_supported(a, bits, G))
+        return QMM_ERR_UNSUPPORTED;
+    for (int m0 = 0; m0 < M; m0 += kMaxRowsPerLaunch) {
+        const qmm::ProductArgs b = qmm::rows_of(a, m0, M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch);
+        if (qmm::launch_mfma_tiled(b, bits, G, stream) != hipSuccess)
+            return QMM_ERR_LAUNCH;
+    }
+    return QMM_OK;
+}
+
 int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,
                        const uint16_t *scales, const uint16_t *biases, float *y, int M, int K,
                        int N, int bits, int G, hipStream_t stream)

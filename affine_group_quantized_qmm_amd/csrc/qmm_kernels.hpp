@@ -85,6 +85,15 @@ bool mfma_supported(int bits, int G);  // whether launch_mfma handles (bits, G)
 // and its launcher (hipErrorInvalidValue when it cannot).
 bool mfma_xr_supported(const ProductArgs &a, int bits, int G);
 hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// Tiled (MFMA-native) weight layout: whether the product on it supports
+// the shape (bits 2, 4, 8; K*bits a multiple of 512; K/G a multiple of 4;
+// parts that fit), the repack from the standard layout (N padded to whole
+// 16-row tiles with zeros) and the product (a.wq = tiled codes, a.scales =
+// tiled (s, b) words; 16 rows per launch at most).
+bool tiled_supported(const ProductArgs &a, int bits, int G);
+hipError_t launch_repack_tiled(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases, uint8_t *tw,
+                               uint32_t *tsb, int N, int K, int bits, int G, hipStream_t stream);
+hipError_t launch_mfma_tiled(const ProductArgs &a, int bits, int G, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size_t count,
                                 hipStream_t stream);
 

@@ -33,6 +33,8 @@
 #include "qmm_device.hpp"
 #include "qmm_kernels.hpp"
 
+#include <type_traits>
+
 namespace qmm {
 namespace {
 
@@ -101,27 +103,44 @@ __device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int g
 // (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), at least as
 // large as the group-sum scratch of the start (XG x 64 floats), then two
 // buffers of kXrBatch tiles of partial sums.
-template <int BITS, int G, int XC>
+// (The tiled-layout variant keeps its weights in registers: only the group-
+// sum scratch.)
+template <int BITS, int G, int XC, bool TILED = false>
 __host__ __device__ constexpr size_t xr_wave_lds()
 {
     using Geo = XrGeo<BITS, G, XC>;
-    const size_t run = 16 * (size_t)Geo::LSTR + 16 * 4 * (size_t)Geo::SBSTR;
+    const size_t run = TILED ? 0 : 16 * (size_t)Geo::LSTR + 16 * 4 * (size_t)Geo::SBSTR;
     const size_t xs = (size_t)Geo::XG * 4 * 16 * sizeof(float);
     return run > xs ? run : xs;
 }
-template <int BITS, int G, int XC>
+template <int BITS, int G, int XC, bool TILED = false>
 __host__ __device__ constexpr size_t xr_lds_bytes(int KP)
 {
-    return (size_t)KP * xr_wave_lds<BITS, G, XC>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
+    return (size_t)KP * xr_wave_lds<BITS, G, XC, TILED>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
 }
+
+// Tiled (MFMA-native) layout, for codes whose lane chunk (the G/4 codes lane
+// block c takes of a group: G*bits/32 bytes) is a whole number of 16-bit
+// halves: 2, 4 and 8 bits. Per 16-row tile t, lane L = 16c + i owns the
+// stream of row 16t + i's chunks c of groups 0, 1, 2, ..., cut into 16-byte
+// units; unit u of lane L of tile t sits at byte ((t*UB + u)*64 + L)*16,
+// UB = K*bits/512. Scales and biases: word (s | b << 16) of row 16t + i and
+// group g at word ((t*Kg/4 + g/4)*16 + i)*4 + g%4. Rows past N hold zeros.
+template <int BITS, int G>
+__host__ __device__ constexpr int tiled_chunk_bytes() { return G * BITS / 32; }
 
 // SBW: bytes per scale/bias load (4: two groups per load, 2: one group).
 // NST: tiles of loads in flight per wave (register stages).
 // FUSED: the launch runs several projections (tile -> projection lookup).
-template <int BITS, int G, int XC, int SBW, int NST, bool FUSED>
+// TILED: weights in the tiled layout above (a.wq: codes, a.scales: the
+// (s, b) words); each lane loads its MFMA operands directly and nothing of
+// the weights goes through LDS.
+template <int BITS, int G, int XC, int SBW, int NST, bool FUSED, bool TILED = false>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
     using Geo = XrGeo<BITS, G, XC>;
+    constexpr int CB = tiled_chunk_bytes<BITS, G>();       // tiled: bytes per lane chunk
+    constexpr int NIT = (Geo::XG * CB + 15) / 16;          // tiled: 16-byte code loads per lane per tile
     constexpr int T = Geo::T, CH = Geo::CH, GB = Geo::GB, XG = Geo::XG, NI = Geo::NI;
     constexpr int LSTR = Geo::LSTR, SBSTR = Geo::SBSTR, NWR = Geo::NWR, NWC = Geo::NWC;
     constexpr int SBE = SBW / 2;                             // groups per scale/bias load
@@ -133,10 +152,10 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     const int lane = threadIdx.x % kWave;
     const int kp = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int KP = blockDim.x / kWave;
-    uint8_t *const wmy = xr_lds + (size_t)kp * xr_wave_lds<BITS, G, XC>();
+    uint8_t *const wmy = xr_lds + (size_t)kp * xr_wave_lds<BITS, G, XC, TILED>();
     uint32_t *const sbmy = reinterpret_cast<uint32_t *>(wmy + 16 * LSTR);
     // red[buf][slot][part][r][lane]
-    float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G, XC>());
+    float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G, XC, TILED>());
     auto red_at = [&](int buf, int slot, int part, int r) -> float & {
         return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
     };
@@ -183,10 +202,20 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         scol[j] = e % V;
     }
 
-    struct Stage {
+    struct StageStd {
         u32x4 w[NI];
         uint32_t s[NS], b[NS];
     };
+    struct StageTiled {
+        u32x4 w[NIT];
+        u32x4 sb[Geo::XQ];
+    };
+    using Stage = std::conditional_t<TILED, StageTiled, StageStd>;
+    // tiled: this part's first 16-byte unit and group quad, and their counts
+    // (parts start on whole units and quads)
+    const uint32_t UB = (uint32_t)K * BITS / 512;
+    const int u0 = pb * CB / 16, nu_part = max(ng * CB / 16, 1);
+    const int q0 = pb / 4, nq = max(ng / 4, 1);
     // Loads of one tile. Past the workgroup's last tile every lane reads the
     // first 16 bytes of that tile instead (one cache line, never used), so
     // the loads stay unconditional without streaming a tile twice.
@@ -195,28 +224,44 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         // loads makes the compiler drain every load in flight
         uint32_t keep = tile >= t1 ? 0u : ~0u;
         pin_register(keep);
-        const Slab sl = slab_at(min(tile, t1 - 1));
-        const int rmax = sl.p.N - 1 - sl.tile * 16;  // rows past N re-read row N-1
-        const uint8_t *wt = reinterpret_cast<const uint8_t *>(sl.p.wq) + (size_t)sl.tile * 16 * RB;
+        if constexpr (TILED) {
+            const int tc = min(tile, t1 - 1);
+            const uint8_t *tw = reinterpret_cast<const uint8_t *>(a.wq) + (size_t)tc * UB * 1024;
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const uint32_t off = ((uint32_t)min(wr[j], rmax) * RB + wcol[j]) & keep;
-            st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(wt + off));
-        }
-        const size_t sbase = (size_t)sl.tile * 16 * Kg + pb;
+            for (int j = 0; j < NIT; ++j) {
+                const uint32_t off = ((uint32_t)((u0 + min(j, nu_part - 1)) * 64 + lane) * 16) & keep;
+                st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(tw + off));
+            }
+            const uint32_t *tsb = reinterpret_cast<const uint32_t *>(a.scales) + (size_t)tc * (Kg / 4) * 64;
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const uint32_t off = ((uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE) & keep;
-            if constexpr (SBW == 4) {
-                st.s[j] = *reinterpret_cast<const uint32_t *>(sl.p.scales + sbase + off);
-                st.b[j] = *reinterpret_cast<const uint32_t *>(sl.p.biases + sbase + off);
-            } else {
-                st.s[j] = sl.p.scales[sbase + off];
-                st.b[j] = sl.p.biases[sbase + off];
+            for (int u = 0; u < Geo::XQ; ++u) {
+                const uint32_t off = ((uint32_t)((q0 + min(u, nq - 1)) * 16 + i) * 4) & keep;
+                st.sb[u] = *reinterpret_cast<const u32x4 *>(tsb + off);
+            }
+        } else {
+            const Slab sl = slab_at(min(tile, t1 - 1));
+            const int rmax = sl.p.N - 1 - sl.tile * 16;  // rows past N re-read row N-1
+            const uint8_t *wt = reinterpret_cast<const uint8_t *>(sl.p.wq) + (size_t)sl.tile * 16 * RB;
+    #pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const uint32_t off = ((uint32_t)min(wr[j], rmax) * RB + wcol[j]) & keep;
+                st.w[j] = load_weight(reinterpret_cast<const u32x4 *>(wt + off));
+            }
+            const size_t sbase = (size_t)sl.tile * 16 * Kg + pb;
+    #pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const uint32_t off = ((uint32_t)min(sr[j], rmax) * Kg + scol[j] * SBE) & keep;
+                if constexpr (SBW == 4) {
+                    st.s[j] = *reinterpret_cast<const uint32_t *>(sl.p.scales + sbase + off);
+                    st.b[j] = *reinterpret_cast<const uint32_t *>(sl.p.biases + sbase + off);
+                } else {
+                    st.s[j] = sl.p.scales[sbase + off];
+                    st.b[j] = sl.p.biases[sbase + off];
+                }
             }
         }
     };
-    auto stage_to_lds = [&](Stage &st) {
+    auto stage_to_lds = [&](StageStd &st) {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
             *reinterpret_cast<u32x4 *>(wmy + wl[j]) = st.w[j];
@@ -286,8 +331,9 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         }
         // scale/bias words of groups past the part stay zero: those groups
         // (computed in whole quads) contribute nothing
-        for (int e = lane; e < 16 * SBSTR; e += kWave)
-            sbmy[e] = 0u;
+        if constexpr (!TILED)
+            for (int e = lane; e < 16 * SBSTR; e += kWave)
+                sbmy[e] = 0u;
     }
 
     const int chunk_byte = c * (Geo::CHB / 8);
@@ -297,11 +343,16 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
 
     auto process = [&](Stage &sk, int tile) {
         __builtin_amdgcn_sched_barrier(0);
-        stage_to_lds(sk);
-        // the stage's registers are free again: start the loads NST tiles ahead
-        issue(sk, tile + NST);
-        if (tile >= t1)  // uniform over the workgroup: a round's tail past the range
+        if constexpr (!TILED) {
+            stage_to_lds(sk);
+            // the stage's registers are free again: start the loads NST tiles ahead
+            issue(sk, tile + NST);
+        }
+        if (tile >= t1) {  // uniform over the workgroup: a round's tail past the range
+            if constexpr (TILED)
+                issue(sk, tile + NST);
             return;
+        }
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < Geo::XQ; ++u) {
@@ -313,18 +364,28 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     const int g = 4 * u + t;
                     P[t] = float4_t{0.f, 0.f, 0.f, 0.f};
                     if (g < XG) {  // compile-time after unrolling
-                        uint32_t raw[NWR];
-#pragma unroll
-                        for (int w = 0; w < NWR; ++w)
-                            raw[w] = *reinterpret_cast<const uint32_t *>(wrow_lds + g * GB + 4 * w);
                         uint32_t chunk[NWC];
+                        if constexpr (TILED) {
+                            // group g's chunk: bytes g*CB .. g*CB+CB-1 of the lane's part stream
 #pragma unroll
-                        for (int w = 0; w < NWC; ++w) {
-                            if constexpr (Geo::SHIFT == 0)
-                                chunk[w] = raw[w];
-                            else
-                                chunk[w] = w + 1 < NWR ? __builtin_amdgcn_alignbit(raw[w + 1], raw[w], chunk_shift)
-                                                       : (raw[w] >> chunk_shift);
+                            for (int w = 0; w < NWC; ++w) {
+                                const int d = (g * CB) / 4 + w;  // compile-time
+                                const uint32_t v = sk.w[d / 4][d % 4];
+                                chunk[w] = CB >= 4 ? v : (v >> (8 * ((g * CB) % 4)));
+                            }
+                        } else {
+                            uint32_t raw[NWR];
+#pragma unroll
+                            for (int w = 0; w < NWR; ++w)
+                                raw[w] = *reinterpret_cast<const uint32_t *>(wrow_lds + g * GB + 4 * w);
+#pragma unroll
+                            for (int w = 0; w < NWC; ++w) {
+                                if constexpr (Geo::SHIFT == 0)
+                                    chunk[w] = raw[w];
+                                else
+                                    chunk[w] = w + 1 < NWR ? __builtin_amdgcn_alignbit(raw[w + 1], raw[w], chunk_shift)
+                                                           : (raw[w] >> chunk_shift);
+                            }
                         }
                         half2_t q[CH / 2];
                         unpack_pairs<BITS, CH>(chunk, q);
@@ -337,12 +398,19 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     }
                 }
                 // bias term of the quad: one fp32 MFMA over its 4 groups
-                const uint32_t sbo = sbrow[4 * u + c];
+                uint32_t sbo;
+                u32x4 sbq;
+                if constexpr (TILED) {
+                    sbq = sk.sb[u];
+                    sbo = c == 0 ? sbq[0] : c == 1 ? sbq[1] : c == 2 ? sbq[2] : sbq[3];
+                } else {
+                    sbo = sbrow[4 * u + c];
+                    sbq = *reinterpret_cast<const u32x4 *>(sbrow + 4 * u);
+                }
                 const float so = half_bits_to_float((uint16_t)(sbo & 0xffffu));
                 const float bo = half_bits_to_float((uint16_t)(sbo >> 16)) - CodeOffset<BITS>::value * so;
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsa[u], bo, acc, 0, 0, 0);
                 // scale term: acc += s[n][g] * P_g
-                const u32x4 sbq = *reinterpret_cast<const u32x4 *>(sbrow + 4 * u);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     if (4 * u + t < XG) {
@@ -379,6 +447,8 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 }
             }
         }
+        if constexpr (TILED)  // the stage's registers are consumed: the loads NST tiles ahead
+            issue(sk, tile + NST);
     };
 
     // Rounds of NST tiles, one per stage. Every round stages and reloads all
@@ -524,6 +594,154 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Tiled layout: repack and the product on it.
+// ---------------------------------------------------------------------------
+
+// One thread per output byte of the tiled codes: byte p of unit u of lane
+// L = 16c + i of tile t is byte (16u + p) of that lane's stream, i.e. byte
+// (16u + p) % CB of group g = (16u + p) / CB's chunk c of row 16t + i, whose
+// codes start at stream bit (g*G + c*G/4)*BITS of the row.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t *__restrict__ wq,
+                                                           uint8_t *__restrict__ out, int N, int K,
+                                                           size_t total)
+{
+    constexpr int CB = tiled_chunk_bytes<BITS, G>();
+    const uint32_t UB = (uint32_t)K * BITS / 512;
+    const size_t wpr = (size_t)K * BITS / 32;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int p = (int)(idx % 16);
+        const int L = (int)((idx / 16) % 64);
+        const size_t tu = idx / 1024;  // t * UB + u
+        const size_t t = tu / UB;
+        const int u = (int)(tu % UB);
+        const int c = L / 16, i = L % 16;
+        const size_t n = t * 16 + i;
+        uint8_t v = 0;
+        if (n < (size_t)N) {
+            const int sb = 16 * u + p;  // byte of the lane stream
+            const int g = sb / CB;
+            const size_t bit = ((size_t)g * G + (size_t)c * (G / 4)) * BITS + (size_t)(sb % CB) * 8;
+            const uint32_t *row = wq + n * wpr;
+            v = (uint8_t)((row[bit / 32] >> (bit % 32)) & 0xffu);  // 8-bit aligned: never straddles words
+        }
+        out[idx] = v;
+    }
+}
+
+// One thread per output word of the tiled (s, b) words.
+__global__ __launch_bounds__(256) void repack_sb_kernel(const uint16_t *__restrict__ scales,
+                                                        const uint16_t *__restrict__ biases,
+                                                        uint32_t *__restrict__ out, int N, int Kg,
+                                                        size_t total)
+{
+    const int Kq = Kg / 4;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int e = (int)(idx % 4);
+        const int i = (int)((idx / 4) % 16);
+        const size_t tq = idx / 64;  // t * Kq + q
+        const size_t t = tq / Kq;
+        const int g = (int)(tq % Kq) * 4 + e;
+        const size_t n = t * 16 + i;
+        uint32_t v = 0;
+        if (n < (size_t)N)
+            v = (uint32_t)scales[n * Kg + g] | ((uint32_t)biases[n * Kg + g] << 16);
+        out[idx] = v;
+    }
+}
+
+template <int BITS, int G>
+hipError_t launch_repack_t(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases,
+                           uint8_t *tw, uint32_t *tsb, int N, int K, hipStream_t stream)
+{
+    const size_t tiles = ((size_t)N + 15) / 16;
+    const size_t wbytes = tiles * 16 * (size_t)K * BITS / 8;
+    const size_t sbwords = tiles * 16 * (size_t)(K / G);
+    auto grid = [](size_t work) {
+        const size_t b = (work + 255) / 256;
+        return dim3((unsigned)(b < 65536 ? (b ? b : 1) : 65536));
+    };
+    hipLaunchKernelGGL((repack_codes_kernel<BITS, G>), grid(wbytes), dim3(256), 0, stream, wq, tw, N, K, wbytes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(repack_sb_kernel, grid(sbwords), dim3(256), 0, stream, scales, biases, tsb, N, K / G,
+                       sbwords);
+    return hipGetLastError();
+}
+
+// The product on tiled weights: parts must start on whole 16-byte units of
+// the lane streams and on whole group quads.
+template <int BITS, int G, int XC>
+bool plan_xr_tiled(const ProductArgs &a, XrPlan &plan)
+{
+    using Geo = XrGeo<BITS, G, XC>;
+    constexpr int CB = tiled_chunk_bytes<BITS, G>();
+    const int Kg = a.K / G;
+    if (((long long)a.K * BITS) % 512 != 0 || Kg % 4 != 0 || a.split != 1)
+        return false;
+    const int gran = CB >= 4 ? 4 : 16 / CB;
+    const int per_part = Geo::XG / gran;
+    if (per_part < 1)
+        return false;
+    const int nu = Kg / gran;
+    const int KP = (nu + per_part - 1) / per_part;
+    if (KP > kXrMaxParts || KP > nu || ((nu + KP - 1) / KP) * gran > Geo::XG)
+        return false;
+    plan = XrPlan{KP, gran, 4};
+    return true;
+}
+
+template <int BITS, int G, int XC>
+hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
+{
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16};
+    const int per_cu = kXrMaxParts / plan.KP;
+    const long long want = (long long)device_cu_count() * per_cu;
+    const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
+    const size_t lds = xr_lds_bytes<BITS, G, XC, true>(plan.KP);
+    constexpr int NST = 2;
+    static bool allowed = false;
+    if (!allowed) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)xr_lds_bytes<BITS, G, XC, true>(kXrMaxParts));
+        if (e != hipSuccess)
+            return e;
+        allowed = true;
+    }
+    hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>), dim3(gx), dim3(plan.KP * kWave), lds,
+                       stream, xa);
+    return hipGetLastError();
+}
+
+template <int BITS, int G>
+hipError_t launch_xr_tiled_t(const ProductArgs &a, hipStream_t stream, bool &done)
+{
+    XrPlan plan;
+    done = true;
+    if (plan_xr_tiled<BITS, G, xr_small_codes<BITS>()>(a, plan))
+        return launch_xr_tiled_variant<BITS, G, xr_small_codes<BITS>()>(a, plan, stream);
+    if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>()) {
+        if (plan_xr_tiled<BITS, G, xr_large_codes<BITS>()>(a, plan))
+            return launch_xr_tiled_variant<BITS, G, xr_large_codes<BITS>()>(a, plan, stream);
+    }
+    done = false;
+    return hipSuccess;
+}
+
+template <int BITS, int G>
+bool tiled_supported_t(const ProductArgs &a)
+{
+    XrPlan plan;
+    if (plan_xr_tiled<BITS, G, xr_small_codes<BITS>()>(a, plan))
+        return true;
+    return plan_xr_tiled<BITS, G, xr_large_codes<BITS>()>(a, plan);
+}
+
 }  // namespace
 
 bool mfma_xr_supported(const ProductArgs &a, int bits, int G)
@@ -555,6 +773,41 @@ hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t str
     QMM_XR_CASE(6, 32) QMM_XR_CASE(6, 64) QMM_XR_CASE(6, 128)
     QMM_XR_CASE(8, 32) QMM_XR_CASE(8, 64) QMM_XR_CASE(8, 128)
 #undef QMM_XR_CASE
+    if (e == hipSuccess && !done)
+        return hipErrorInvalidValue;
+    return e;
+}
+
+#define QMM_TILED_CASES(X) \
+    X(2, 32) X(2, 64) X(2, 128) X(4, 32) X(4, 64) X(4, 128) X(8, 32) X(8, 64) X(8, 128)
+
+bool tiled_supported(const ProductArgs &a, int bits, int G)
+{
+#define QMM_TS(B, GG) \
+    if (bits == B && G == GG) return tiled_supported_t<B, GG>(a);
+    QMM_TILED_CASES(QMM_TS)
+#undef QMM_TS
+    return false;
+}
+
+hipError_t launch_repack_tiled(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases, uint8_t *tw,
+                               uint32_t *tsb, int N, int K, int bits, int G, hipStream_t stream)
+{
+#define QMM_RP(B, GG) \
+    if (bits == B && G == GG) return launch_repack_t<B, GG>(wq, scales, biases, tw, tsb, N, K, stream);
+    QMM_TILED_CASES(QMM_RP)
+#undef QMM_RP
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_tiled(const ProductArgs &a, int bits, int G, hipStream_t stream)
+{
+    bool done = false;
+    hipError_t e = hipErrorInvalidValue;
+#define QMM_TL(B, GG) \
+    if (bits == B && G == GG) e = launch_xr_tiled_t<B, GG>(a, stream, done);
+    QMM_TILED_CASES(QMM_TL)
+#undef QMM_TL
     if (e == hipSuccess && !done)
         return hipErrorInvalidValue;
     return e;

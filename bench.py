@@ -15,9 +15,10 @@ call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 Prints one JSON line. Synthetic data (seeded; no trained weights). Besides
 the headline cells the line carries `layer`: one decoder layer of the layer
 sweep at M = 1 and 8, its seven projections launched one by one and with
-q/k/v and gate/up fused (qmm_forward_fused); and `other_workloads`: the
+q/k/v and gate/up fused (qmm_forward_fused); `other_workloads`: the
 dense up projection with 2- and 3-bit codes and the mixed 5/6/8-bit G=64
-projections, timed like the headline cells.
+projections, timed like the headline cells; and `tiled_layout`: the
+headline cells read from the tiled layout (qmm_forward_tiled).
 
 The roofline object covers the kernel that takes most of a step. Its
 `traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE and
@@ -305,6 +306,43 @@ def measure_cells(qmm, shape, Ms, dev, stream, capture):
     return out
 
 
+def measure_tiled(qmm, shape, Ms, dev, stream, capture):
+    """The headline projection read from the tiled (matrix-core) layout:
+    qmm_repack_tiled once per weight copy (untimed), qmm_forward_tiled timed."""
+    p = qmm_inputs.make_problem(seed=0, M=max(Ms), K=shape.K, N=shape.N, bits=shape.bits, G=shape.G,
+                                packed_words=True)
+    wq = torch.from_numpy(p.words.view(np.int32)).to(dev)
+    s = torch.from_numpy(p.scales).to(dev)
+    b = torch.from_numpy(p.biases).to(dev)
+    copies = max(2, -(-ROTATION_BYTES // shape.weight_bytes))
+    first = qmm.qmm_repack_tiled(wq, s, b, shape.bits, shape.G)
+    sets = [first] + [(first[0].clone(), first[1].clone()) for _ in range(copies - 1)]
+    del wq, s, b
+    x = torch.from_numpy(p.x).to(dev)
+    out = {"workload": f"{shape.name} from the tiled layout (qmm_forward_tiled)",
+           "weight_copies_rotated": copies}
+    for M in Ms:
+        xm = x[:M].contiguous()
+        y = torch.empty((M, shape.N), dtype=torch.float32, device=dev)
+
+        def call(i, xm=xm, y=y):
+            tw, tsb = sets[i % copies]
+            qmm.qmm_forward_tiled(xm, tw, tsb, shape.N, shape.bits, shape.G, out=y)
+
+        reps = max(50, 2 * copies)
+        g = capture(call, reps)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
+        del g
+        out[f"M{M}"] = {
+            "us_per_call": round(ms * 1e3, 3),
+            "weight_GBps": round(shape.weight_bytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * shape.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        }
+    return out
+
+
 def measure_layer(qmm, dev, stream, capture):
     """One decoder layer of the layer sweep (q, k, v, o, gate, up, down; 4-bit
     G=32) at each sweep M: the seven projections one launch each, and with
@@ -503,6 +541,7 @@ def main():
         out["layer"] = measure_layer(qmm, dev, stream, capture)
         out["other_workloads"] = {sh.name: measure_cells(qmm, sh, Ms, dev, stream, capture)
                                   for sh, Ms in EXTRA_SHAPES}
+        out["tiled_layout"] = measure_tiled(qmm, shape, CELLS_M, dev, stream, capture)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, shape, args.cpu_rows)
     print(json.dumps(out), flush=True)

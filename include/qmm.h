@@ -161,6 +161,41 @@ int qmm_forward_fused(const uint16_t *x, int count, const uint32_t *const *wq,
                       float *const *y, const int *N, int M, int K, int bits, int G,
                       hipStream_t stream);
 
+/*
+ * Tiled (MFMA-native) weight layout: an optional offline re-layout of the
+ * packed weights for the multi-row matrix-core path. The vmlx-swift pull
+ * request #565 page tiles the weights of its lane matmul modules (commit
+ * "LaneQMM", "Tiling policy") and keeps the packed layout for the readers
+ * that consume it directly; here too the tiled copy is read only by
+ * qmm_forward_tiled, and qmm_forward keeps reading the packed layout.
+ *
+ * Layout, for bits in {2, 4, 8}, G in {32, 64, 128}, K a multiple of 4*G with
+ * K*bits a multiple of 512; rows grouped in 16-row tiles (N padded with zero
+ * rows). Lane L = 16c + i (c = 0..3, i = 0..15) of tile t owns the bit stream
+ * made of chunk c of every group of row 16t + i, in group order, where chunk
+ * c of a group is its codes c*G/4 .. c*G/4 + G/4 - 1 in the packed bit order;
+ * the stream is cut into 16-byte units and unit u of lane L of tile t is
+ * stored at byte ((t*UB + u)*64 + L)*16 of tiled_w, UB = K*bits/512.
+ * tiled_sb holds uint32 words (scale | bias << 16) (fp16 bit patterns): row
+ * 16t + i, group g at word ((t*(K/G)/4 + g/4)*16 + i)*4 + g%4.
+ *
+ * qmm_tiled_bytes: bytes of tiled_w, and of tiled_sb in *sb_bytes (if not
+ * NULL); 0 (and 0) when the layout does not exist for (N, K, bits, G).
+ * qmm_repack_tiled: writes both from the packed wq, scales, biases (device
+ * memory, caller-owned, 16-byte aligned); QMM_ERR_UNSUPPORTED when the layout
+ * does not exist for the shape. Async on `stream`.
+ * qmm_forward_tiled: y[M,N] = x . W^T from the tiled form; the arguments
+ * mean what they mean for qmm_forward. It runs the multi-row matrix-core
+ * kernel for every M (16 rows per launch); QMM_ERR_UNSUPPORTED when K is
+ * too long for it (more than 8 parts of 768 activations, 512 for 8 bits).
+ */
+size_t qmm_tiled_bytes(int N, int K, int bits, int G, size_t *sb_bytes);
+int qmm_repack_tiled(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases,
+                     uint8_t *tiled_w, uint32_t *tiled_sb, int N, int K, int bits, int G,
+                     hipStream_t stream);
+int qmm_forward_tiled(const uint16_t *x, const uint8_t *tiled_w, const uint32_t *tiled_sb,
+                      float *y, int M, int K, int N, int bits, int G, hipStream_t stream);
+
 /* Bytes of workspace qmm_forward_splitk needs: split_k * M * N * 4 for
  * split_k >= 2, 0 for split_k == 1 and for invalid arguments. */
 size_t qmm_splitk_workspace_bytes(int M, int N, int split_k);

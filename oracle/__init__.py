@@ -60,6 +60,8 @@ class Oracle:
         lib.qo_forward_factored.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.qo_forward_factored.restype = ctypes.c_int
+        lib.qo_repack_tiled.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int]
+        lib.qo_repack_tiled.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -92,6 +94,22 @@ class Oracle:
         if rc:
             raise ValueError(f"qo_unpack failed ({rc})")
         return codes
+
+    def repack_tiled(self, words, scales, biases, K: int, bits: int, G: int):
+        """The tiled layout of packed weights: (codes as uint8 [Np*K*bits/8],
+        (s | b << 16) words as uint32 [Np*K/G]), Np = N rounded up to 16."""
+        words = np.ascontiguousarray(words, dtype=np.uint32)
+        s = np.ascontiguousarray(scales, dtype=np.float16).view(np.uint16)
+        b = np.ascontiguousarray(biases, dtype=np.float16).view(np.uint16)
+        N = words.shape[0]
+        Np = (N + 15) // 16 * 16
+        tw = np.empty(Np * K * bits // 8, dtype=np.uint8)
+        tsb = np.empty(Np * (K // G), dtype=np.uint32)
+        rc = self.lib.qo_repack_tiled(words.ctypes.data, s.ctypes.data, b.ctypes.data,
+                                      tw.ctypes.data, tsb.ctypes.data, N, K, bits, G)
+        if rc:
+            raise ValueError(f"qo_repack_tiled failed ({rc})")
+        return tw, tsb
 
     # -- products ----------------------------------------------------------
     @staticmethod

@@ -268,3 +268,50 @@ int qo_forward_factored(const uint16_t *x, const uint32_t *words, const uint16_t
 {
     return run_forward(x, words, s, b, y, NULL, M, K, N, bits, G, nthreads, 1, NULL, 0);
 }
+
+/* ---------------------------------------------------------------------
+ * Tiled layout (an optional re-layout of the packed weights, defined by
+ * this library for its matrix-core path; the vmlx-swift pull request #565
+ * page tiles its lane-matmul weights, commit "LaneQMM" and its tiling
+ * policy, without printing a layout). Rows come in tiles of 16 (N padded
+ * with zero rows). Code k of row n belongs to tile t = n/16, row i = n%16
+ * of it, group g = k/G, lane block c = (k mod G)/(G/4), position
+ * j = k mod (G/4) in that block's chunk. Lane L = 16c + i of tile t owns a
+ * bit stream holding, for g = 0, 1, ..., the chunk c of group g; the code's
+ * bits start at stream bit (g*(G/4) + j)*bits. Stream bit p is bit p mod 8 of
+ * byte ((t*UB + p/128)*64 + L)*16 + (p mod 128)/8, UB = K*bits/512.
+ * Scales and biases become words s | b<<16 (the fp16 bit patterns): row n,
+ * group g at word ((t*(K/G)/4 + g/4)*16 + i)*4 + g mod 4.
+ * The function scatters every code bit and every (s, b) pair to its place.
+ * ------------------------------------------------------------------- */
+int qo_repack_tiled(const uint32_t *words, const uint16_t *s, const uint16_t *b, uint8_t *tw,
+                    uint32_t *tsb, int64_t N, int64_t K, int bits, int G)
+{
+    if (bits < 1 || bits > 8 || G < 4 || G % 4 || N < 1 || K < G || K % (4 * G) ||
+        (K * bits) % 512)
+        return -1;
+    const int64_t W = K * bits / 32, Kg = K / G, UB = K * bits / 512;
+    const int64_t Np = (N + 15) / 16 * 16;
+    memset(tw, 0, (size_t)(Np * K * bits / 8));
+    memset(tsb, 0, (size_t)(Np * Kg) * sizeof(uint32_t));
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t t = n / 16, i = n % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            const uint32_t q = read_code(words + n * W, k, bits);
+            const int64_t g = k / G, c = (k % G) / (G / 4), j = k % (G / 4);
+            const int64_t L = 16 * c + i;
+            for (int e = 0; e < bits; ++e) {
+                if (!((q >> e) & 1u))
+                    continue;
+                const int64_t p = (g * (G / 4) + j) * bits + e;
+                const int64_t byte = ((t * UB + p / 128) * 64 + L) * 16 + (p % 128) / 8;
+                tw[byte] |= (uint8_t)(1u << (p % 8));
+            }
+        }
+        for (int64_t g = 0; g < Kg; ++g)
+            tsb[((t * (Kg / 4) + g / 4) * 16 + i) * 4 + g % 4] =
+                (uint32_t)s[n * Kg + g] | ((uint32_t)b[n * Kg + g] << 16);
+    }
+    return 0;
+}
+

@@ -333,9 +333,52 @@ def absum(o) -> list[str]:
     return fails
 
 
+def tiled_layout(o) -> list[str]:
+    """The tiled re-layout, checked against word-level closed forms that follow
+    from its definition for each supported width at G = 32: lane block c of a
+    group is word c of the group's 4 words (4-bit), words 2c, 2c+1 of its 8
+    (8-bit), the 16-bit half c of its 2 words (2-bit); a lane's 16-byte unit
+    holds consecutive groups; rows past N are zero; (s, b) words are the
+    scales and biases of 4 consecutive groups per row, rows of a tile in order."""
+    fails = []
+    rng = np.random.default_rng(21)
+    N, K, G = 37, 512, 32
+    for bits in (2, 4, 8):
+        W = K * bits // 32
+        words = rng.integers(0, 1 << 32, size=(N, W), dtype=np.uint32)
+        s = rng.random((N, K // G)).astype(np.float16)
+        b = (rng.random((N, K // G)) - 0.5).astype(np.float16)
+        tw, tsb = o.repack_tiled(words, s, b, K, bits, G)
+        UB = K * bits // 512
+        tiles = (N + 15) // 16
+        units = tw.view(np.uint32).reshape(tiles, UB, 4, 16, 4)  # [t][u][c][i][dword]
+        padded = np.zeros((tiles * 16, W), dtype=np.uint32)
+        padded[:N] = words
+        rows = padded.reshape(tiles, 16, W)  # [t][i][word]
+        wpg = G * bits // 32  # words per group
+        if bits == 4:    # unit u: groups 4u..4u+3, word c of each
+            want = rows.reshape(tiles, 16, UB, 4, 4)[:, :, :, :, :]  # [t][i][u][group in unit][word c]
+            want = want.transpose(0, 2, 4, 1, 3)                    # [t][u][c][i][group in unit]
+        elif bits == 8:  # unit u: groups 2u, 2u+1, words 2c, 2c+1 of each
+            g8 = rows.reshape(tiles, 16, UB, 2, 4, 2)                # [t][i][u][group][c][half]
+            want = g8.transpose(0, 2, 4, 1, 3, 5).reshape(tiles, UB, 4, 16, 4)
+        else:            # bits 2: unit u: groups 8u..8u+7, 16-bit half c of each group's 2 words
+            halves = rows.reshape(tiles, 16, UB, 8, wpg).view(np.uint16).reshape(tiles, 16, UB, 8, 4)
+            want = halves.transpose(0, 2, 4, 1, 3).copy().view(np.uint32)  # pairs of halves -> dwords
+        if not np.array_equal(units, want):
+            fails.append(f"tiled codes bits={bits}: {int((units != want).sum())} words differ")
+        sbw = tsb.reshape(tiles, K // G // 4, 16, 4)            # [t][q][i][e]
+        sp = np.zeros((tiles * 16, K // G), dtype=np.uint32)
+        sp[:N] = s.view(np.uint16).astype(np.uint32) | (b.view(np.uint16).astype(np.uint32) << 16)
+        want_sb = sp.reshape(tiles, 16, K // G // 4, 4).transpose(0, 2, 1, 3)
+        if not np.array_equal(sbw, want_sb):
+            fails.append(f"tiled (s, b) words bits={bits}: {int((sbw != want_sb).sum())} differ")
+    return fails
+
+
 ALL_PINS = (half_decode, pack_golden, single_code, round_trip, forward_golden,
             integer_matmul, dyadic_exhaustive, one_hot, ones, zero_codes,
-            linearity, row_invariance, absum)
+            linearity, row_invariance, absum, tiled_layout)
 
 
 def run_all(o) -> dict[str, list[str]]:

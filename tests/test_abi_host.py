@@ -119,3 +119,18 @@ def test_fused_rejects_before_launch():
     assert lib.qmm_forward_fused(4096, 2, odd, good, good, good, ns, 1, 64, 4, 32, None) == -7
     null_p = (ctypes.c_void_p * 2)(4096, None)
     assert lib.qmm_forward_fused(4096, 2, good, good, null_p, good, ns, 1, 64, 4, 32, None) == -1
+
+
+def test_tiled_sizes_and_rejections():
+    """Sizes of the tiled layout, and shapes it does not exist for, on the host."""
+    assert qmm.qmm_tiled_bytes(17408, 5120, 4, 32) == (17408 * 5120 // 2, 17408 * 160 * 4)
+    assert qmm.qmm_tiled_bytes(20, 512, 8, 32) == (32 * 512, 32 * 16 * 4)  # rows padded to 32
+    for args in ((100, 5120, 5, 32), (100, 5120, 6, 64), (16, 416, 4, 32), (16, 192, 8, 64)):
+        assert qmm.qmm_tiled_bytes(*args) == (0, 0), args
+    lib = qmm._lib
+    assert lib.qmm_repack_tiled(None, 16, 16, 16, 16, 16, 512, 4, 32, None) == -1
+    assert lib.qmm_repack_tiled(16, 16, 16, 16, 16, 16, 512, 5, 32, None) == -9
+    assert lib.qmm_repack_tiled(16, 16, 16, 16, 24, 16, 512, 4, 32, None) == -7
+    assert lib.qmm_forward_tiled(16, 16, 16, 16, 1, 512, 16, 3, 32, None) == -9
+    assert lib.qmm_forward_tiled(16, 16, 16, 16, 1, 416, 16, 4, 32, None) == -9
+    assert lib.qmm_forward_tiled(16, 16, None, 16, 1, 512, 16, 4, 32, None) == -1

@@ -12,6 +12,15 @@ import oracle
 from tests import _pins
 
 MUTANTS = [
+    ("tiled layout: lane block and row swapped",
+     "const int64_t L = 16 * c + i;",
+     "const int64_t L = 4 * i + c;"),
+    ("tiled layout: groups not in stream order",
+     "const int64_t p = (g * (G / 4) + j) * bits + e;",
+     "const int64_t p = ((g ^ 1) * (G / 4) + j) * bits + e;"),
+    ("tiled (s, b) words: scale and bias halves swapped",
+     "(uint32_t)s[n * Kg + g] | ((uint32_t)b[n * Kg + g] << 16);",
+     "(uint32_t)b[n * Kg + g] | ((uint32_t)s[n * Kg + g] << 16);"),
     ("unpack MSB-first within a word",
      "return (int)((row[t / 32] >> (t % 32)) & 1u);",
      "return (int)((row[t / 32] >> (31 - t % 32)) & 1u);"),
