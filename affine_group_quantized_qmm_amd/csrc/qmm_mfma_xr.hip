@@ -42,19 +42,20 @@ constexpr int kXrMaxParts = 8;    // waves (K parts) per workgroup
 constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after one barrier
 
 // Activations per row held by one wave (XC: 640 or 768, 512 for 8-bit codes,
-// i.e. 80 to 96 registers of A operands) and tiles of loads in flight per
-// wave (register stages), as the registers allow. The host takes the first
-// variant of a width whose parts fit the workgroup (xr_variants).
-constexpr int xr_stages(int bits, int xc)
-{
-    return bits <= 4 ? (xc <= 640 ? 3 : 2) : bits == 8 ? 2 : (xc <= 640 ? 2 : 1);
-}
-// Two-byte scale/bias loads (odd group counts) take twice the load registers:
-// one stage fewer, so that no variant spills.
-constexpr int xr_stages_sbw(int bits, int xc, int sbw)
-{
-    return sbw == 4 || xr_stages(bits, xc) == 1 ? xr_stages(bits, xc) : xr_stages(bits, xc) - 1;
-}
+// i.e. 80 to 96 registers of A operands). The host takes the first variant
+// of a width whose parts fit the workgroup (xr_variants).
+//
+// Tiles of loads in flight per wave (register stages): one. A stage's
+// registers are free again as soon as its tile is in LDS, so the next
+// tile's loads stream during the computation even with one stage; more
+// stages only make the first burst of requests larger, and every wave's
+// first tile then lands later in it. Measured on the 5120 x 17408 4-bit
+// projection: 22.1 / 23.6 us (M = 4 / 16) with three stages, 20.6 / 22.6 with
+// two, 18.4 / 21.4 with one.
+#ifndef XR_STD_STAGES
+#define XR_STD_STAGES 1
+#endif
+constexpr int xr_stages_sbw(int, int, int) { return XR_STD_STAGES; }
 
 template <int BITS, int G, int XC>
 struct XrGeo {
@@ -695,6 +696,19 @@ bool plan_xr_tiled(const ProductArgs &a, XrPlan &plan)
     return true;
 }
 
+#ifndef XR_TILED_NST3
+#define XR_TILED_NST3 2
+#endif
+// Register stages of the tiled variant: three while the stages and the
+// activation registers stay within 200 VGPRs, else two.
+template <int BITS, int G, int XC>
+constexpr int xr_tiled_stages()
+{
+    using Geo = XrGeo<BITS, G, XC>;
+    constexpr int per_stage = 4 * ((Geo::XG * tiled_chunk_bytes<BITS, G>() + 15) / 16 + Geo::XQ);
+    return 3 * per_stage + 4 * Geo::XG * Geo::T <= 200 ? XR_TILED_NST3 : 2;
+}
+
 template <int BITS, int G, int XC>
 hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
@@ -703,7 +717,7 @@ hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hip
     const long long want = (long long)device_cu_count() * per_cu;
     const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
     const size_t lds = xr_lds_bytes<BITS, G, XC, true>(plan.KP);
-    constexpr int NST = 2;
+    constexpr int NST = xr_tiled_stages<BITS, G, XC>();
     static bool allowed = false;
     if (!allowed) {
         const hipError_t e = hipFuncSetAttribute(
