@@ -33,6 +33,7 @@ _p, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _lib.qmm_pack.argtypes = [_p, _p, _i, _i, _i, _p]
 _lib.qmm_forward.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_rowexact.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_forward_bf16.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
 _lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_fused.argtypes = [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
@@ -47,12 +48,13 @@ _lib.qmm_strerror.argtypes = [_i]
 _lib.qmm_strerror.restype = ctypes.c_char_p
 _lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
 _lib.qmm_kernel_name.restype = ctypes.c_char_p
-for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_splitk,
+for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_bf16,
+           _lib.qmm_forward_splitk,
            _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_repack_tiled,
            _lib.qmm_forward_tiled, _lib.qmm_validate):
     _f.restype = _i
 
-EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_splitk",
+EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_bf16", "qmm_forward_splitk",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
             "qmm_forward_kernel", "qmm_forward_fused", "qmm_tiled_bytes", "qmm_repack_tiled",
             "qmm_forward_tiled")
@@ -111,7 +113,7 @@ def _check(t: torch.Tensor, name: str, dtypes, shape, device) -> None:
 _WORD_DTYPES = (torch.int32, torch.uint32)
 
 
-def _operands(x, wq, scales, biases, bits, G):
+def _operands(x, wq, scales, biases, bits, G, dtype=torch.float16):
     if x.dim() != 2 or wq.dim() != 2:
         raise ValueError("x and wq must be 2-D")
     M, K = x.shape
@@ -119,10 +121,10 @@ def _operands(x, wq, scales, biases, bits, G):
     if K % G or (K * bits) % 32:
         raise ValueError("K must be a multiple of G (and K*bits of 32)")
     dev = x.device
-    _check(x, "x", (torch.float16,), (M, K), None)
+    _check(x, "x", (dtype,), (M, K), None)
     _check(wq, "wq", _WORD_DTYPES, (N, K * bits // 32), dev)
-    _check(scales, "scales", (torch.float16,), (N, K // G), dev)
-    _check(biases, "biases", (torch.float16,), (N, K // G), dev)
+    _check(scales, "scales", (dtype,), (N, K // G), dev)
+    _check(biases, "biases", (dtype,), (N, K // G), dev)
     return M, K, N, dev
 
 
@@ -166,6 +168,20 @@ def qmm_forward_rowexact(x, wq, scales, biases, bits: int, G: int, out=None) -> 
                                    biases.data_ptr(), out.data_ptr(), M, K, N, bits, G, _stream(x))
     if rc:
         raise QmmError(rc, "qmm_forward_rowexact")
+    return out
+
+
+def qmm_forward_bf16(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Tensor:
+    """The product with bfloat16 x, scales and biases (fp32 y); every row is
+    bitwise equal to the call on that row alone."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G, dtype=torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    rc = _lib.qmm_forward_bf16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+                               biases.data_ptr(), out.data_ptr(), M, K, N, bits, G, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_bf16")
     return out
 
 

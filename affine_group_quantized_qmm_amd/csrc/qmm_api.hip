@@ -93,7 +93,7 @@ int launch_args(Kernel kind, const qmm::ProductArgs &full, int bits, int G, hipS
         const qmm::ProductArgs a = qmm::rows_of(full, m0, M - m0 < step ? M - m0 : step);
         hipError_t e;
         switch (kind) {
-        case Kernel::qmv: e = qmm::launch_qmv(a, bits, G, stream); break;
+        case Kernel::qmv: e = qmm::launch_qmv(a, bits, G, false, stream); break;
         case Kernel::mfma: e = qmm::launch_mfma_xr(a, bits, G, stream); break;
         default: e = qmm::launch_mfma(a, bits, G, stream); break;
         }
@@ -220,6 +220,22 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
     if (rc != QMM_OK)
         return rc;
     return launch_product(Kernel::qmv, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
+}
+
+int qmm_forward_bf16(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                     const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
+                     hipStream_t stream)
+{
+    const int rc = qmm_validate(x, wq, scales, biases, y, M, K, N, bits, G, 0, nullptr, 0);
+    if (rc != QMM_OK)
+        return rc;
+    const qmm::ProductArgs full = product_args(x, wq, scales, biases, y, M, K, N, 1);
+    for (int m0 = 0; m0 < M; m0 += kQmvRowsPerLaunch) {
+        const qmm::ProductArgs a = qmm::rows_of(full, m0, M - m0 < kQmvRowsPerLaunch ? M - m0 : kQmvRowsPerLaunch);
+        if (qmm::launch_qmv(a, bits, G, true, stream) != hipSuccess)
+            return QMM_ERR_LAUNCH;
+    }
+    return QMM_OK;
 }
 
 int qmm_forward_fused(const uint16_t *x, int count, const uint32_t *const *wq,

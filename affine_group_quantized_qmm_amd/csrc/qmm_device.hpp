@@ -188,6 +188,86 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&
 }
 
 // ---------------------------------------------------------------------------
+// bf16 widening (activations, scales and biases in bf16).
+//
+// A bf16 number has 7 fraction bits. 4-bit codes use the exponent trick of
+// the fp16 route with the code in fraction bits 3..6 under 2^4, so a half
+// becomes 16 + code exactly; pairs are again codes (k, k + 4) of a word (four
+// shifts and four v_and_or_b32 per word) and the epilogue folds the 16 into
+// the bias. Other widths do not fit a 7-bit fraction with a usable pairing
+// (8-bit codes not at all): each code is extracted, converted to fp32 and two
+// codes are packed to bf16 with round-to-nearest, exact because every code is
+// an integer below 2^8. Those pairs hold consecutive codes (2i, 2i + 1).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int P>
+__device__ __forceinline__ bf16x2_t code_pair4_bf16(uint32_t word)
+{
+    constexpr uint32_t mask = 0x00780078u;   // fraction bits 3..6 of each half
+    constexpr uint32_t magic = 0x41804180u;  // 2^4 in each half
+    uint32_t v;
+    if constexpr (P == 0)
+        v = word << 3;
+    else if constexpr (P == 1)
+        v = word >> 1;
+    else if constexpr (P == 2)
+        v = word >> 5;
+    else
+        v = word >> 9;
+    return __builtin_bit_cast(bf16x2_t, and_or(v, mask, magic));
+}
+
+// Code k of a run of codes stored from bit 0 of w.
+template <int BITS, int K, int NW>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW])
+{
+    static_assert(K * BITS + BITS <= 32 * NW, "code past the loaded words");
+    return stream_window<K * BITS>(w) & ((1u << BITS) - 1u);
+}
+
+template <int BITS>
+struct CodeOffsetBf16 {
+    static constexpr float value = BITS == 4 ? 16.0f : 0.0f;
+};
+
+template <int BITS, int NW, int... Ps>
+__device__ __forceinline__ void unpack_pairs_bf16_impl(const uint32_t (&w)[NW], bf16x2_t *out,
+                                                       std::integer_sequence<int, Ps...>)
+{
+    if constexpr (BITS == 4)
+        ((out[Ps] = code_pair4_bf16<Ps % 4>(w[Ps / 4])), ...);
+    else
+        ((out[Ps] = bf16x2_t{(__bf16)(float)code_at<BITS, 2 * Ps>(w),
+                             (__bf16)(float)code_at<BITS, 2 * Ps + 1>(w)}), ...);
+}
+
+// Widen NCODES codes into NCODES/2 bf16 pairs: 16 + code in pair order for
+// 4 bits, exact codes in natural order otherwise.
+template <int BITS, int NCODES, int NW>
+__device__ __forceinline__ void unpack_pairs_bf16(const uint32_t (&w)[NW], bf16x2_t (&out)[NCODES / 2])
+{
+    static_assert(NCODES % 8 == 0, "runs of whole 8-code units");
+    unpack_pairs_bf16_impl<BITS, NW>(w, out, std::make_integer_sequence<int, NCODES / 2>{});
+}
+
+// The 8 activations of a unit (bf16 bit patterns) in the order of
+// unpack_pairs_bf16: pair order for 4-bit codes, natural otherwise.
+template <int BITS>
+__device__ __forceinline__ half8_t to_pair_order_bf16(half8_t v)
+{
+    if constexpr (BITS == 4)
+        return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
+    else
+        return v;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h16)
+{
+    return __builtin_bit_cast(float, h16 << 16);
+}
+
+// ---------------------------------------------------------------------------
 // Loads of NW consecutive words with a known byte alignment. Packed weights
 // are read once per call, so the loads carry the non-temporal hint unless
 // QMM_WEIGHT_LOADS_NT is defined to 0.

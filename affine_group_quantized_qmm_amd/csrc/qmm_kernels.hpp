@@ -78,7 +78,8 @@ inline ProductArgs rows_of(const ProductArgs &a, int m0, int count)
 // runtime's error) and hipErrorInvalidValue for an unsupported (bits, G).
 hipError_t launch_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,
                        hipStream_t stream);
-hipError_t launch_qmv(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// bf16: x, scales and biases are bf16 bit patterns instead of fp16.
+hipError_t launch_qmv(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream);
 hipError_t launch_mfma(const ProductArgs &a, int bits, int G, hipStream_t stream);
 bool mfma_supported(int bits, int G);  // whether launch_mfma handles (bits, G)
 // Register-resident multi-row kernel: whether it can run `a` (split included)

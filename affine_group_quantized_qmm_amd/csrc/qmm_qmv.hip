@@ -43,7 +43,9 @@ constexpr int chunk_limit(int mr) { return mr == 1 ? kMaxChunkK : 2 * kMaxChunkK
 // arithmetic of the one-row launch (same lane-to-group map, same dot and
 // epilogue sequence, same reduction tree), so with the same LPR each row of
 // an MR-row result is bitwise equal to that row computed alone.
-template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR>
+// BF16: x, scales and biases hold bf16 bit patterns (codes widened to bf16
+// and dotted with v_dot2_f32_bf16) instead of fp16.
+template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR, bool BF16>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
     constexpr int NWG = G * BITS / 32;        // words per group
@@ -165,16 +167,25 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             const int vv = (int)threadIdx.x + t * kThreads;
             const int m = vv / XUNITS, u = vv % XUNITS;
             const half8_t v = xreg[t];
+            // sum of the unit's 8 activations (fp32 accumulation of pairs)
             float s8 = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s8 += (float)v[e];
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (BF16) {
+                    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+                    s8 = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2_t, half2_t{v[2 * e], v[2 * e + 1]}), ones, s8, false);
+                } else {
+                    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+                    s8 = __builtin_amdgcn_fdot2(half2_t{v[2 * e], v[2 * e + 1]}, ones, s8, false);
+                }
+            }
             // the UPG units of a group sit in consecutive lanes
 #pragma unroll
             for (int off = 1; off < UPG; off *= 2)
                 s8 += __shfl_xor(s8, off);
             if (m < MR && u < ng * UPG) {
-                xp[m][u % UPG][u / UPG] = to_pair_order<BITS>(v);
+                xp[m][u % UPG][u / UPG] = BF16 ? to_pair_order_bf16<BITS>(v) : to_pair_order<BITS>(v);
                 if (u % UPG == 0)
                     xsum[m][u / UPG] = s8;
             }
@@ -218,21 +229,36 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             if (sl * LPR < ng) {
                 const int gl = lam + sl * LPR;
                 const int glc = min(gl, ng - 1);
-                half2_t q[NPAIR];
-                unpack_pairs<BITS, G>(st.w, q);
                 const uint32_t sb = sbl[wave * RPW + r * RPI + rho][glc];
-                const float sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
-                const float bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
+                float sc, bias;
+                if constexpr (BF16) {
+                    sc = bf16_bits_to_float(sb & 0xffffu);
+                    bias = bf16_bits_to_float(sb >> 16) - CodeOffsetBf16<BITS>::value * sc;
+                } else {
+                    sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
+                    bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
+                }
+                half2_t q[NPAIR];
+                bf16x2_t qb[NPAIR];
+                if constexpr (BF16)
+                    unpack_pairs_bf16<BITS, G>(st.w, qb);
+                else
+                    unpack_pairs<BITS, G>(st.w, q);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     float P = 0.f;
 #pragma unroll
                     for (int u = 0; u < UPG; ++u) {
                         const half8_t xv = xp[m][u][glc];
-                        P = __builtin_amdgcn_fdot2(q[4 * u + 0], half2_t{xv[0], xv[1]}, P, false);
-                        P = __builtin_amdgcn_fdot2(q[4 * u + 1], half2_t{xv[2], xv[3]}, P, false);
-                        P = __builtin_amdgcn_fdot2(q[4 * u + 2], half2_t{xv[4], xv[5]}, P, false);
-                        P = __builtin_amdgcn_fdot2(q[4 * u + 3], half2_t{xv[6], xv[7]}, P, false);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const half2_t xe = {xv[2 * e], xv[2 * e + 1]};
+                            if constexpr (BF16)
+                                P = __builtin_amdgcn_fdot2_f32_bf16(qb[4 * u + e], __builtin_bit_cast(bf16x2_t, xe), P,
+                                                                    false);
+                            else
+                                P = __builtin_amdgcn_fdot2(q[4 * u + e], xe, P, false);
+                        }
                     }
                     // explicit fma: the same rounding in every instantiation
                     const float contrib = __builtin_fmaf(sc, P, bias * xsum[m][glc]);
@@ -270,12 +296,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     }
 }
 
-template <int BITS, int G, int LPR, int SLOTS, int RPW = kRowsPerWave, int PD_ROWS = kPrefetchRows, int MR = 1>
+template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR, bool BF16>
 hipError_t launch_qmv_slots(const ProductArgs &a, hipStream_t stream)
 {
     const int rows_per_block = kWaves * RPW;
     const dim3 grid((a.N + rows_per_block - 1) / rows_per_block, 1, a.split);
-    hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS, MR>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS, MR, BF16>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -293,7 +319,7 @@ int qmv_lanes_per_row(int slice)
     return slice <= max_slots1 * kWave && half % 2 == 1 ? 32 : 64;
 }
 
-template <int BITS, int G, int LPR, int MR, int S>
+template <int BITS, int G, int LPR, int MR, int S, bool BF16>
 hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
 {
     // PD: with 32 lanes per row both row groups of a wave stay in flight
@@ -302,14 +328,14 @@ hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
     constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
     if constexpr (S > 1) {
         if (slots >= S)
-            return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR>(a, stream);
-        return launch_qmv_upto<BITS, G, LPR, MR, S - 1>(a, slots, stream);
+            return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR, BF16>(a, stream);
+        return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, stream);
     } else {
-        return launch_qmv_slots<BITS, G, LPR, 1, kRowsPerWave, PDR, MR>(a, stream);
+        return launch_qmv_slots<BITS, G, LPR, 1, kRowsPerWave, PDR, MR, BF16>(a, stream);
     }
 }
 
-template <int BITS, int G, int MR>
+template <int BITS, int G, int MR, bool BF16>
 hipError_t launch_qmv_rows(const ProductArgs &a, hipStream_t stream)
 {
     const int Kg = a.K / G;
@@ -319,11 +345,11 @@ hipError_t launch_qmv_rows(const ProductArgs &a, hipStream_t stream)
     if (lpr == 32) {
         constexpr int max_s = chunk_limit(MR) / (MR * 32 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8)>(a, need, stream);
+            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8), BF16>(a, need, stream);
     } else {
         constexpr int max_s = chunk_limit(MR) / (MR * 64 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4)>(a, need, stream);
+            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4), BF16>(a, need, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -339,7 +365,7 @@ int qmv_max_rows(int lpr)
 }
 
 // Up to 8 rows (a.M <= 8), in as few launches as the chunk size allows.
-template <int BITS, int G>
+template <int BITS, int G, bool BF16>
 hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
 {
     const int Kg = a.K / G;
@@ -348,10 +374,10 @@ hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
     for (int m0 = 0; m0 < a.M; m0 += cap) {
         const ProductArgs b = rows_of(a, m0, a.M - m0 < cap ? a.M - m0 : cap);
         hipError_t e;
-        if (b.M <= 1) e = launch_qmv_rows<BITS, G, 1>(b, stream);
-        else if (b.M <= 2) e = launch_qmv_rows<BITS, G, 2>(b, stream);
-        else if (b.M <= 4) e = launch_qmv_rows<BITS, G, 4>(b, stream);
-        else e = launch_qmv_rows<BITS, G, 8>(b, stream);
+        if (b.M <= 1) e = launch_qmv_rows<BITS, G, 1, BF16>(b, stream);
+        else if (b.M <= 2) e = launch_qmv_rows<BITS, G, 2, BF16>(b, stream);
+        else if (b.M <= 4) e = launch_qmv_rows<BITS, G, 4, BF16>(b, stream);
+        else e = launch_qmv_rows<BITS, G, 8, BF16>(b, stream);
         if (e != hipSuccess)
             return e;
     }
@@ -360,10 +386,10 @@ hipError_t launch_qmv_t(const ProductArgs &a, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_qmv(const ProductArgs &a, int bits, int G, hipStream_t stream)
+hipError_t launch_qmv(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream)
 {
 #define QMM_QMV_CASE(B, GG) \
-    if (bits == B && G == GG) return launch_qmv_t<B, GG>(a, stream);
+    if (bits == B && G == GG) return bf16 ? launch_qmv_t<B, GG, true>(a, stream) : launch_qmv_t<B, GG, false>(a, stream);
     QMM_QMV_CASE(2, 32) QMM_QMV_CASE(2, 64) QMM_QMV_CASE(2, 128)
     QMM_QMV_CASE(3, 32) QMM_QMV_CASE(3, 64) QMM_QMV_CASE(3, 128)
     QMM_QMV_CASE(4, 32) QMM_QMV_CASE(4, 64) QMM_QMV_CASE(4, 128)

@@ -18,7 +18,8 @@ sweep at M = 1 and 8, its seven projections launched one by one and with
 q/k/v and gate/up fused (qmm_forward_fused); `other_workloads`: the
 dense up projection with 2- and 3-bit codes and the mixed 5/6/8-bit G=64
 projections, timed like the headline cells; and `tiled_layout`: the
-headline cells read from the tiled layout (qmm_forward_tiled).
+headline cells read from the tiled layout (qmm_forward_tiled); and `bf16`:
+the headline cells with bfloat16 x, scales and biases (qmm_forward_bf16).
 
 The roofline object covers the kernel that takes most of a step. Its
 `traffic` (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE and
@@ -272,16 +273,23 @@ EXTRA_SHAPES = ((W.Shape("dense_up_5120x17408_w2g32", K=5120, N=17408, bits=2, G
                 *((sh, W.MIXED_M) for sh in W.MIXED))
 
 
-def measure_cells(qmm, shape, Ms, dev, stream, capture):
-    """Per-M launch times of qmm_forward on `shape` (rotated weight copies, graph replay)."""
+def measure_cells(qmm, shape, Ms, dev, stream, capture, dtype="f16"):
+    """Per-M launch times of qmm_forward (qmm_forward_bf16 for dtype "bf16") on
+    `shape` (rotated weight copies, graph replay)."""
     p = qmm_inputs.make_problem(seed=5, M=max(Ms), K=shape.K, N=shape.N, bits=shape.bits,
-                                G=shape.G, packed_words=True)
+                                G=shape.G, packed_words=True, dtype=dtype)
+
+    def operand(a):
+        if dtype == "bf16":  # uint16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
     wq = torch.from_numpy(p.words.view(np.int32)).to(dev)
-    s = torch.from_numpy(p.scales).to(dev)
-    b = torch.from_numpy(p.biases).to(dev)
+    s = operand(p.scales)
+    b = operand(p.biases)
     copies = max(2, -(-ROTATION_BYTES // shape.weight_bytes))
     sets = [(wq, s, b)] + [(wq.clone(), s.clone(), b.clone()) for _ in range(copies - 1)]
-    x = torch.from_numpy(p.x).to(dev)
+    x = operand(p.x)
+    fwd = qmm.qmm_forward_bf16 if dtype == "bf16" else qmm.qmm_forward
     out = {"K": shape.K, "N": shape.N, "bits": shape.bits, "G": shape.G,
            "weight_bytes_per_call": shape.weight_bytes, "weight_copies_rotated": copies}
     for M in Ms:
@@ -289,7 +297,7 @@ def measure_cells(qmm, shape, Ms, dev, stream, capture):
         y = torch.empty((M, shape.N), dtype=torch.float32, device=dev)
 
         def call(i, xm=xm, y=y):
-            qmm.qmm_forward(xm, *sets[i % copies], shape.bits, shape.G, out=y)
+            fwd(xm, *sets[i % copies], shape.bits, shape.G, out=y)
 
         reps = max(50, 2 * copies)
         g = capture(call, reps)
@@ -298,7 +306,8 @@ def measure_cells(qmm, shape, Ms, dev, stream, capture):
         ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
         del g
         out[f"M{M}"] = {
-            "kernel": qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G),
+            "kernel": "qmv" if dtype == "bf16" else qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits,
+                                                                        shape.G),
             "us_per_call": round(ms * 1e3, 3),
             "weight_GBps": round(shape.weight_bytes / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * shape.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
@@ -542,6 +551,8 @@ def main():
         out["other_workloads"] = {sh.name: measure_cells(qmm, sh, Ms, dev, stream, capture)
                                   for sh, Ms in EXTRA_SHAPES}
         out["tiled_layout"] = measure_tiled(qmm, shape, CELLS_M, dev, stream, capture)
+        out["bf16"] = {"workload": f"{shape.name} with bfloat16 x, scales and biases (qmm_forward_bf16)",
+                       **measure_cells(qmm, shape, CELLS_M, dev, stream, capture, dtype="bf16")}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, shape, args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -38,6 +38,9 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 
 
+DTYPES = {"f16": 0, "bf16": 1}  # operand types of x, scales and biases
+
+
 class Oracle:
     """ctypes view of one compiled oracle library."""
 
@@ -47,6 +50,8 @@ class Oracle:
         lib.qo_half_to_double.restype = ctypes.c_double
         lib.qo_half_array_to_double.argtypes = [_p, _p, _i64]
         lib.qo_half_array_to_double.restype = None
+        lib.qo_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.qo_bf16_to_double.restype = ctypes.c_double
         lib.qo_pack.argtypes = [_p, _p, _i64, _i64, ctypes.c_int]
         lib.qo_pack.restype = ctypes.c_int
         lib.qo_unpack.argtypes = [_p, _p, _i64, _i64, ctypes.c_int]
@@ -57,6 +62,13 @@ class Oracle:
         lib.qo_forward_rows.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
                                         ctypes.c_int, ctypes.c_int, _p, _i64, ctypes.c_int]
         lib.qo_forward_rows.restype = ctypes.c_int
+        lib.qo_forward_ex.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.qo_forward_ex.restype = ctypes.c_int
+        lib.qo_forward_rows_ex.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
+                                           ctypes.c_int, ctypes.c_int, _p, _i64, ctypes.c_int,
+                                           ctypes.c_int]
+        lib.qo_forward_rows_ex.restype = ctypes.c_int
         lib.qo_forward_factored.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.qo_forward_factored.restype = ctypes.c_int
@@ -113,40 +125,55 @@ class Oracle:
 
     # -- products ----------------------------------------------------------
     @staticmethod
-    def _operands(x, words, scales, biases):
-        x = np.ascontiguousarray(x, dtype=np.float16)
+    def _operands(x, words, scales, biases, dtype="f16"):
+        """fp16 operands as float16 arrays; bf16 operands as uint16 bit patterns."""
+        if dtype not in DTYPES:
+            raise ValueError(f"dtype must be one of {tuple(DTYPES)}")
+        t = np.float16 if dtype == "f16" else np.uint16
+        x = np.ascontiguousarray(x, dtype=t)
         words = np.ascontiguousarray(words, dtype=np.uint32)
-        scales = np.ascontiguousarray(scales, dtype=np.float16)
-        biases = np.ascontiguousarray(biases, dtype=np.float16)
+        scales = np.ascontiguousarray(scales, dtype=t)
+        biases = np.ascontiguousarray(biases, dtype=t)
         return x, words, scales, biases
 
-    def forward(self, x, words, scales, biases, bits: int, G: int, nthreads: int | None = None):
-        """Dequantize-then-dot. Returns (y, A) as float64 [M, N]; A = sum_k |w x|."""
-        x, words, scales, biases = self._operands(x, words, scales, biases)
+    def bf16_to_double(self, h: np.ndarray) -> np.ndarray:
+        """bfloat16 bit patterns (uint16) -> float64, elementwise."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        out = np.empty(h.shape, dtype=np.float64)
+        flat, o = h.ravel(), out.ravel()
+        for i in range(flat.size):
+            o[i] = self.lib.qo_bf16_to_double(int(flat[i]))
+        return out
+
+    def forward(self, x, words, scales, biases, bits: int, G: int, nthreads: int | None = None,
+                dtype: str = "f16"):
+        """Dequantize-then-dot. Returns (y, A) as float64 [M, N]; A = sum_k |w x|.
+        dtype "bf16": x, scales and biases are bfloat16 bit patterns (uint16)."""
+        x, words, scales, biases = self._operands(x, words, scales, biases, dtype)
         M, K = x.shape
         N = words.shape[0]
         y = np.empty((M, N), dtype=np.float64)
         a = np.empty((M, N), dtype=np.float64)
-        rc = self.lib.qo_forward(x.ctypes.data, words.ctypes.data, scales.ctypes.data,
-                                 biases.ctypes.data, y.ctypes.data, a.ctypes.data,
-                                 M, K, N, bits, G, nthreads or default_threads())
+        rc = self.lib.qo_forward_ex(x.ctypes.data, words.ctypes.data, scales.ctypes.data,
+                                    biases.ctypes.data, y.ctypes.data, a.ctypes.data,
+                                    M, K, N, bits, G, DTYPES[dtype], nthreads or default_threads())
         if rc:
             raise ValueError(f"qo_forward failed ({rc})")
         return y, a
 
     def forward_rows(self, x, words, scales, biases, bits: int, G: int, rows,
-                     nthreads: int | None = None):
+                     nthreads: int | None = None, dtype: str = "f16"):
         """Like ``forward`` for the listed output rows only: (y, A) are [M, len(rows)]."""
-        x, words, scales, biases = self._operands(x, words, scales, biases)
+        x, words, scales, biases = self._operands(x, words, scales, biases, dtype)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         M, K = x.shape
         N = words.shape[0]
         y = np.empty((M, rows.size), dtype=np.float64)
         a = np.empty((M, rows.size), dtype=np.float64)
-        rc = self.lib.qo_forward_rows(x.ctypes.data, words.ctypes.data, scales.ctypes.data,
-                                      biases.ctypes.data, y.ctypes.data, a.ctypes.data,
-                                      M, K, N, bits, G, rows.ctypes.data, rows.size,
-                                      nthreads or default_threads())
+        rc = self.lib.qo_forward_rows_ex(x.ctypes.data, words.ctypes.data, scales.ctypes.data,
+                                         biases.ctypes.data, y.ctypes.data, a.ctypes.data,
+                                         M, K, N, bits, G, rows.ctypes.data, rows.size,
+                                         DTYPES[dtype], nthreads or default_threads())
         if rc:
             raise ValueError(f"qo_forward_rows failed ({rc})")
         return y, a

@@ -12,6 +12,7 @@
  *                      bit t is bit (t mod 32) of word t/32 (least
  *                      significant bit first).
  *   weight  w[n,k]   = s[n, k/G] * q[n,k] + b[n, k/G]
+ *           (x, s and b are fp16, or all three bf16 in the _ex entry points)
  *   output  y[m,n]   = sum over k = 0..K-1, ascending, of w[n,k] * x[m,k]
  *   bound   A[m,n]   = sum over k of |w[n,k] * x[m,k]|
  *
@@ -61,6 +62,41 @@ void qo_half_array_to_double(const uint16_t *h, double *out, int64_t count)
 {
     for (int64_t i = 0; i < count; ++i)
         out[i] = qo_half_to_double(h[i]);
+}
+
+/* ---------------------------------------------------------------------
+ * bfloat16 -> double (exact). A bfloat16 is the upper half of an IEEE 754
+ * binary32: 1 sign bit, 8 exponent bits (bias 127) and 7 fraction bits;
+ * exponent 0 encodes zero and subnormals (fraction * 2^-133), exponent 255
+ * encodes inf and NaN.
+ * ------------------------------------------------------------------- */
+double qo_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 7) & 0xff;
+    int frac = h & 0x7f;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -133);
+    else if (expo == 255)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + frac), expo - 134);
+    return sign ? -v : v;
+}
+
+/* Operand types of x, scales and biases. */
+enum { QO_F16 = 0, QO_BF16 = 1 };
+
+static double decode(int dtype, uint16_t h)
+{
+    return dtype == QO_BF16 ? qo_bf16_to_double(h) : qo_half_to_double(h);
+}
+
+static void decode_array(int dtype, const uint16_t *h, double *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = decode(dtype, h[i]);
 }
 
 /* ---------------------------------------------------------------------
@@ -122,6 +158,7 @@ struct job {
     double *y, *absum;
     int64_t M, K, N;
     int bits, G, factored;
+    int dtype; /* QO_F16 or QO_BF16: type of x, s and b */
     int64_t n_begin, n_end;
     const int64_t *rows; /* optional list of output rows; y/absum are then [M, nrows] */
     int64_t out_stride;  /* row stride of y/absum: N, or nrows with a list */
@@ -137,14 +174,14 @@ static void rows_dequant_dot(const struct job *jb)
     const int64_t Kg = K / G, W = K * jb->bits / 32;
     double *w = (double *)malloc((size_t)K * sizeof(double));
     double *xd = (double *)malloc((size_t)(M * K) * sizeof(double));
-    qo_half_array_to_double(jb->x, xd, M * K);
+    decode_array(jb->dtype, jb->x, xd, M * K);
     for (int64_t i = jb->n_begin; i < jb->n_end; ++i) {
         const int64_t n = job_row(jb, i);
         const uint32_t *row = jb->words + n * W;
         for (int64_t k = 0; k < K; ++k) {
             double q = (double)read_code(row, k, jb->bits);
-            double s = qo_half_to_double(jb->s[n * Kg + k / G]);
-            double b = qo_half_to_double(jb->b[n * Kg + k / G]);
+            double s = decode(jb->dtype, jb->s[n * Kg + k / G]);
+            double b = decode(jb->dtype, jb->b[n * Kg + k / G]);
             w[k] = s * q + b;
         }
         for (int64_t m = 0; m < M; ++m) {
@@ -170,7 +207,7 @@ static void rows_factored(const struct job *jb)
     const int64_t K = jb->K, M = jb->M, G = jb->G;
     const int64_t Kg = K / G, W = K * jb->bits / 32;
     double *xd = (double *)malloc((size_t)(M * K) * sizeof(double));
-    qo_half_array_to_double(jb->x, xd, M * K);
+    decode_array(jb->dtype, jb->x, xd, M * K);
     for (int64_t i = jb->n_begin; i < jb->n_end; ++i) {
         const int64_t n = job_row(jb, i);
         const uint32_t *row = jb->words + n * W;
@@ -182,8 +219,8 @@ static void rows_factored(const struct job *jb)
                     P += (double)read_code(row, k, jb->bits) * xd[m * K + k];
                     XS += xd[m * K + k];
                 }
-                acc += qo_half_to_double(jb->s[n * Kg + g]) * P
-                     + qo_half_to_double(jb->b[n * Kg + g]) * XS;
+                acc += decode(jb->dtype, jb->s[n * Kg + g]) * P
+                     + decode(jb->dtype, jb->b[n * Kg + g]) * XS;
             }
             jb->y[m * jb->out_stride + i] = acc;
         }
@@ -204,10 +241,12 @@ static void *run_job(void *arg)
 static int run_forward(const uint16_t *x, const uint32_t *words, const uint16_t *s,
                        const uint16_t *b, double *y, double *absum, int64_t M,
                        int64_t K, int64_t N, int bits, int G, int nthreads, int factored,
-                       const int64_t *rows, int64_t nrows)
+                       const int64_t *rows, int64_t nrows, int dtype)
 {
     if (!x || !words || !s || !b || !y)
         return -1;
+    if (dtype != QO_F16 && dtype != QO_BF16)
+        return -2;
     if (M < 1 || K < 1 || N < 1 || G < 1 || K % G || bits < 1 || bits > 8 || (K * bits) % 32)
         return -2;
     const int64_t count = rows ? nrows : N;
@@ -228,6 +267,7 @@ static int run_forward(const uint16_t *x, const uint32_t *words, const uint16_t 
         jb->y = y; jb->absum = absum;
         jb->M = M; jb->K = K; jb->N = N; jb->bits = bits; jb->G = G;
         jb->factored = factored;
+        jb->dtype = dtype;
         jb->rows = rows;
         jb->out_stride = count;
         jb->n_begin = count * t / nthreads;
@@ -247,7 +287,15 @@ int qo_forward(const uint16_t *x, const uint32_t *words, const uint16_t *s, cons
                double *y, double *absum, int64_t M, int64_t K, int64_t N, int bits, int G,
                int nthreads)
 {
-    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, NULL, 0);
+    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, NULL, 0, QO_F16);
+}
+
+/* qo_forward with x, s and b of type dtype (0 fp16, 1 bf16). */
+int qo_forward_ex(const uint16_t *x, const uint32_t *words, const uint16_t *s, const uint16_t *b,
+                  double *y, double *absum, int64_t M, int64_t K, int64_t N, int bits, int G,
+                  int dtype, int nthreads)
+{
+    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, NULL, 0, dtype);
 }
 
 /* Same as qo_forward for a list of output rows only: y and absum are
@@ -259,14 +307,24 @@ int qo_forward_rows(const uint16_t *x, const uint32_t *words, const uint16_t *s,
 {
     if (!rows)
         return -1;
-    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, rows, nrows);
+    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, rows, nrows, QO_F16);
+}
+
+int qo_forward_rows_ex(const uint16_t *x, const uint32_t *words, const uint16_t *s,
+                       const uint16_t *b, double *y, double *absum, int64_t M, int64_t K,
+                       int64_t N, int bits, int G, const int64_t *rows, int64_t nrows,
+                       int dtype, int nthreads)
+{
+    if (!rows)
+        return -1;
+    return run_forward(x, words, s, b, y, absum, M, K, N, bits, G, nthreads, 0, rows, nrows, dtype);
 }
 
 int qo_forward_factored(const uint16_t *x, const uint32_t *words, const uint16_t *s,
                         const uint16_t *b, double *y, int64_t M, int64_t K, int64_t N,
                         int bits, int G, int nthreads)
 {
-    return run_forward(x, words, s, b, y, NULL, M, K, N, bits, G, nthreads, 1, NULL, 0);
+    return run_forward(x, words, s, b, y, NULL, M, K, N, bits, G, nthreads, 1, NULL, 0, QO_F16);
 }
 
 /* ---------------------------------------------------------------------

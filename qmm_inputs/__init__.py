@@ -8,7 +8,9 @@ the computation.
 Every tensor comes from numpy's PCG64 generator (``numpy.random.default_rng``)
 and is drawn in a fixed order: codes (or packed words), scales, biases, x.
 Values are drawn in float64 and rounded once to float16 (round to nearest
-even, numpy's ``astype``).
+even, numpy's ``astype``). For bfloat16 operands (``dtype="bf16"``) the same
+draws are rounded to float32 and then to bfloat16, both to nearest even,
+and kept as uint16 bit patterns (numpy has no bfloat16 type).
 
 Distributions (the workloads described for the verify-block projections in
 the vmlx-swift pull request #565 page, commit "LaneQMM", and the
@@ -53,16 +55,32 @@ def draw_words(rng: np.random.Generator, N: int, K: int, bits: int) -> np.ndarra
     return rng.integers(0, 1 << 32, size=(N, K * bits // 32), dtype=np.uint32)
 
 
-def draw_scales(rng: np.random.Generator, N: int, Kg: int) -> np.ndarray:
-    return rng.uniform(*SCALE_RANGE, size=(N, Kg)).astype(np.float16)
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 (each to nearest even), as uint16 bit
+    patterns. Inputs are finite and far from the float32 limits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
 
 
-def draw_biases(rng: np.random.Generator, N: int, Kg: int) -> np.ndarray:
-    return rng.uniform(*BIAS_RANGE, size=(N, Kg)).astype(np.float16)
+def _round(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return a.astype(np.float16)
+    if dtype == "bf16":
+        return to_bf16_bits(a)
+    raise ValueError("dtype must be 'f16' or 'bf16'")
 
 
-def draw_x(rng: np.random.Generator, M: int, K: int) -> np.ndarray:
-    return rng.standard_normal(size=(M, K)).astype(np.float16)
+def draw_scales(rng: np.random.Generator, N: int, Kg: int, dtype: str = "f16") -> np.ndarray:
+    return _round(rng.uniform(*SCALE_RANGE, size=(N, Kg)), dtype)
+
+
+def draw_biases(rng: np.random.Generator, N: int, Kg: int, dtype: str = "f16") -> np.ndarray:
+    return _round(rng.uniform(*BIAS_RANGE, size=(N, Kg)), dtype)
+
+
+def draw_x(rng: np.random.Generator, M: int, K: int, dtype: str = "f16") -> np.ndarray:
+    return _round(rng.standard_normal(size=(M, K)), dtype)
 
 
 @dataclass
@@ -80,11 +98,12 @@ class Problem:
     biases: np.ndarray
     codes: np.ndarray | None = None
     words: np.ndarray | None = None
+    dtype: str = "f16"  # type of x, scales and biases: "f16" or "bf16" (uint16 bit patterns)
     meta: dict = field(default_factory=dict)
 
 
 def make_problem(seed: int, M: int, K: int, N: int, bits: int, G: int,
-                 packed_words: bool = False) -> Problem:
+                 packed_words: bool = False, dtype: str = "f16") -> Problem:
     if K % G:
         raise ValueError("K must be a multiple of G")
     rng = rng_for(seed)
@@ -94,8 +113,8 @@ def make_problem(seed: int, M: int, K: int, N: int, bits: int, G: int,
     else:
         codes = draw_codes(rng, N, K, bits)
     Kg = K // G
-    scales = draw_scales(rng, N, Kg)
-    biases = draw_biases(rng, N, Kg)
-    x = draw_x(rng, M, K)
+    scales = draw_scales(rng, N, Kg, dtype)
+    biases = draw_biases(rng, N, Kg, dtype)
+    x = draw_x(rng, M, K, dtype)
     return Problem(M=M, K=K, N=N, bits=bits, G=G, seed=seed, x=x,
-                   scales=scales, biases=biases, codes=codes, words=words)
+                   scales=scales, biases=biases, codes=codes, words=words, dtype=dtype)

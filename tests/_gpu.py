@@ -39,17 +39,23 @@ class DeviceProblem:
             else:
                 self.words = o.pack(p.codes, p.bits)
                 self.wq = torch.from_numpy(self.words.view(np.int32)).to(d)
-        self.x = torch.from_numpy(p.x).to(d)
-        self.s = torch.from_numpy(p.scales).to(d)
-        self.b = torch.from_numpy(p.biases).to(d)
+        if p.dtype == "bf16":  # uint16 bit patterns -> torch.bfloat16
+            def dev_bf16(a):
+                return torch.from_numpy(a.view(np.int16)).to(d).view(torch.bfloat16)
+            self.x, self.s, self.b = dev_bf16(p.x), dev_bf16(p.scales), dev_bf16(p.biases)
+        else:
+            self.x = torch.from_numpy(p.x).to(d)
+            self.s = torch.from_numpy(p.scales).to(d)
+            self.b = torch.from_numpy(p.biases).to(d)
 
     def oracle(self, rows=None, m_rows=None):
         o = oracle.get()
         x = self.p.x if m_rows is None else self.p.x[m_rows]
         if rows is None:
-            return o.forward(x, self.words, self.p.scales, self.p.biases, self.p.bits, self.p.G)
+            return o.forward(x, self.words, self.p.scales, self.p.biases, self.p.bits, self.p.G,
+                             dtype=self.p.dtype)
         return o.forward_rows(x, self.words, self.p.scales, self.p.biases, self.p.bits,
-                              self.p.G, rows)
+                              self.p.G, rows, dtype=self.p.dtype)
 
 
 def assert_parity(y, ref, absum, label: str) -> float:

@@ -46,6 +46,55 @@ def _codes_to_words_numpy(codes: np.ndarray, bits: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+def bf16_decode(o) -> list[str]:
+    """Every bfloat16 pattern against numpy's float32 decode of the same bits
+    in the upper half of a binary32."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = o.bf16_to_double(pats)
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns
+        want = (pats.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nan = np.isnan(want)
+    bad = ~((got == want) | (nan & np.isnan(got)))
+    bad |= (want == 0) & (np.signbit(got) != np.signbit(want))
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        return [f"bf16 0x{int(pats[i]):04x}: oracle {got[i]!r}, numpy {want[i]!r} ({int(bad.sum())} bad)"]
+    return []
+
+
+def _bf16_bits_exact(values) -> np.ndarray:
+    """Bit patterns of values that bfloat16 holds exactly (asserted)."""
+    f = np.asarray(values, dtype=np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), f), "value not exact in bf16"
+    return bits
+
+
+def bf16_operands(o) -> list[str]:
+    """Values exact in both fp16 and bf16 (dyadic, few significant bits, in
+    range) give the same product whether x, s and b are passed as fp16 or as
+    bf16: the bf16 path decodes every operand, and each in its own place."""
+    fails = []
+    rng = np.random.default_rng(77)
+    for bits, G, K in ((4, 32, 128), (5, 64, 192), (8, 32, 96)):
+        M, N = 3, 5
+        x = rng.integers(-64, 65, size=(M, K)) / 8.0                 # k/8, |x| <= 8
+        s = rng.integers(1, 17, size=(N, K // G)) * 2.0 ** -9         # j * 2^-9
+        b = rng.integers(-16, 17, size=(N, K // G)) * 2.0 ** -7       # i * 2^-7
+        words = rng.integers(0, 1 << 32, size=(N, K * bits // 32), dtype=np.uint32)
+        y16, a16 = o.forward(_h(x), words, _h(s), _h(b), bits, G)
+        yb, ab = o.forward(_bf16_bits_exact(x), words, _bf16_bits_exact(s), _bf16_bits_exact(b),
+                           bits, G, dtype="bf16")
+        if not (np.array_equal(y16, yb) and np.array_equal(a16, ab)):
+            fails.append(f"bits={bits} G={G}: bf16 and fp16 operands of equal value disagree")
+        rows = np.array([4, 0, 2])
+        yr, _ = o.forward_rows(_bf16_bits_exact(x), words, _bf16_bits_exact(s), _bf16_bits_exact(b),
+                               bits, G, rows, dtype="bf16")
+        if not np.array_equal(yr, y16[:, rows]):
+            fails.append(f"bits={bits} G={G}: bf16 row list disagrees")
+    return fails
+
+
 def half_decode(o) -> list[str]:
     pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     got = o.half_to_double(pats)
@@ -378,7 +427,7 @@ def tiled_layout(o) -> list[str]:
 
 ALL_PINS = (half_decode, pack_golden, single_code, round_trip, forward_golden,
             integer_matmul, dyadic_exhaustive, one_hot, ones, zero_codes,
-            linearity, row_invariance, absum, tiled_layout)
+            linearity, row_invariance, absum, tiled_layout, bf16_decode, bf16_operands)
 
 
 def run_all(o) -> dict[str, list[str]]:

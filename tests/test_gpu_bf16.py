@@ -1,0 +1,79 @@
+"""bfloat16 activations, scales and biases (qmm_forward_bf16) against the fp64
+oracle on the same bf16 bit patterns: every bit width and group size, rows
+1..17 (several 8-row launches), ragged shapes, rows bitwise equal to one-row
+calls, and the dense up projection at full size on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import qmm_inputs
+from qmm_inputs import workloads as W
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+BITS_G = [(b, g) for b in (2, 3, 4, 5, 6, 8) for g in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("bits,G", BITS_G)
+@pytest.mark.parametrize("M", [1, 2, 5, 9])
+def test_bf16_small(bits, G, M):
+    K, N = 13 * G, 200  # ragged per wave and per workgroup
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=900 + M * 7 + bits, M=M, K=K, N=N, bits=bits,
+                                                    G=G, dtype="bf16"))
+    y = _gpu.lib().qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, bits, G)
+    torch.cuda.synchronize()
+    ref, absum = dp.oracle()
+    _gpu.assert_parity(y, ref, absum, f"bf16 bits={bits} G={G} M={M}")
+
+
+@pytest.mark.parametrize("bits,G,K", [(4, 32, 5120), (8, 64, 2048), (5, 64, 2560), (4, 32, 17408),
+                                      (2, 128, 4096), (3, 32, 1280)])
+def test_bf16_rows_bitwise_equal_one_row_calls(bits, G, K):
+    M, N = 17, 150
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=950 + bits, M=M, K=K, N=N, bits=bits, G=G,
+                                                    dtype="bf16"))
+    qmm = _gpu.lib()
+    y = qmm.qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, bits, G)
+    torch.cuda.synchronize()
+    for m in range(M):
+        y1 = qmm.qmm_forward_bf16(dp.x[m:m + 1].contiguous(), dp.wq, dp.s, dp.b, bits, G)
+        torch.cuda.synchronize()
+        assert torch.equal(y[m], y1[0]), f"row {m} of {M} differs from its one-row call"
+    ref, absum = dp.oracle()
+    _gpu.assert_parity(y, ref, absum, f"bf16 rows bits={bits} G={G} K={K}")
+
+
+def test_bf16_one_hot_columns():
+    """x = e_k for every k: y[k, n] = s[n,k/G] q[n,k] + b[n,k/G] (pins the
+    bf16 code widening, its pair order and the scale/bias decode)."""
+    for bits, G in ((4, 32), (5, 64), (8, 32), (2, 64)):
+        K, N = 2 * G, 40
+        p = qmm_inputs.make_problem(seed=5, M=1, K=K, N=N, bits=bits, G=G, dtype="bf16")
+        p.x = qmm_inputs.to_bf16_bits(np.eye(K))
+        p.M = K
+        dp = _gpu.DeviceProblem(p)
+        y = _gpu.lib().qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, bits, G)
+        torch.cuda.synchronize()
+        ref, absum = dp.oracle()
+        _gpu.assert_parity(y, ref, absum, f"bf16 one-hot bits={bits} G={G}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_bf16_dense_up_full_size(M):
+    s = W.DENSE_UP
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=0, M=M, K=s.K, N=s.N, bits=s.bits, G=s.G,
+                                                    packed_words=True, dtype="bf16"))
+    y = _gpu.lib().qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, s.bits, s.G)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([rng.choice(s.N, 256, replace=False), [0, 15, 16, s.N - 1]]))
+    ref, absum = dp.oracle(rows=rows)
+    _gpu.assert_parity(y[:, rows], ref, absum, f"bf16 {s.name} M={M}")
+
+
+def test_bf16_rejects_fp16_tensors():
+    qmm = _gpu.lib()
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=1, M=1, K=64, N=8, bits=4, G=32))
+    with pytest.raises(TypeError):
+        qmm.qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, 4, 32)

@@ -34,11 +34,11 @@ MUTANTS = [
      "c |= (uint32_t)stream_bit(row, k * bits + j) << j;",
      "c |= (uint32_t)stream_bit(row, k * (bits + 1) + j) << j;"),
     ("scale from the wrong group",
-     "double s = qo_half_to_double(jb->s[n * Kg + k / G]);",
-     "double s = qo_half_to_double(jb->s[n * Kg + (k / G + 1) % Kg]);"),
+     "double s = decode(jb->dtype, jb->s[n * Kg + k / G]);",
+     "double s = decode(jb->dtype, jb->s[n * Kg + (k / G + 1) % Kg]);"),
     ("bias group index from k mod Kg",
-     "double b = qo_half_to_double(jb->b[n * Kg + k / G]);",
-     "double b = qo_half_to_double(jb->b[n * Kg + k % Kg]);"),
+     "double b = decode(jb->dtype, jb->b[n * Kg + k / G]);",
+     "double b = decode(jb->dtype, jb->b[n * Kg + k % Kg]);"),
     ("subtracted bias",
      "w[k] = s * q + b;",
      "w[k] = s * q - b;"),
@@ -46,8 +46,8 @@ MUTANTS = [
      "w[k] = s * q + b;",
      "w[k] = s * (q + b);"),
     ("scale and bias swapped",
-     "double s = qo_half_to_double(jb->s[n * Kg + k / G]);\n            double b = qo_half_to_double(jb->b[n * Kg + k / G]);",
-     "double s = qo_half_to_double(jb->b[n * Kg + k / G]);\n            double b = qo_half_to_double(jb->s[n * Kg + k / G]);"),
+     "double s = decode(jb->dtype, jb->s[n * Kg + k / G]);\n            double b = decode(jb->dtype, jb->b[n * Kg + k / G]);",
+     "double s = decode(jb->dtype, jb->b[n * Kg + k / G]);\n            double b = decode(jb->dtype, jb->s[n * Kg + k / G]);"),
     ("dot skips the last k",
      "for (int64_t k = 0; k < K; ++k) {\n                double p",
      "for (int64_t k = 0; k < K - 1; ++k) {\n                double p"),
@@ -67,14 +67,32 @@ MUTANTS = [
      "v = ldexp((double)(1024 + frac), expo - 25);",
      "v = ldexp((double)(1024 + frac), expo - 24);"),
     ("half sign ignored",
-     "return sign ? -v : v;",
-     "return v;"),
+     "v = ldexp((double)(1024 + frac), expo - 25);\n    return sign ? -v : v;",
+     "v = ldexp((double)(1024 + frac), expo - 25);\n    return v;"),
+    ("bf16 sign ignored",
+     "v = ldexp((double)(128 + frac), expo - 134);\n    return sign ? -v : v;",
+     "v = ldexp((double)(128 + frac), expo - 134);\n    return v;"),
     ("factored form: group sum of x counts the codes",
      "XS += xd[m * K + k];",
      "XS += (double)read_code(row, k, jb->bits);"),
     ("factored form: bias times P",
-     "+ qo_half_to_double(jb->b[n * Kg + g]) * XS;",
-     "+ qo_half_to_double(jb->b[n * Kg + g]) * P;"),
+     "+ decode(jb->dtype, jb->b[n * Kg + g]) * XS;",
+     "+ decode(jb->dtype, jb->b[n * Kg + g]) * P;"),
+    ("bf16 exponent bias off by one",
+     "v = ldexp((double)(128 + frac), expo - 134);",
+     "v = ldexp((double)(128 + frac), expo - 133);"),
+    ("bf16 read with an 8-bit fraction",
+     "int frac = h & 0x7f;",
+     "int frac = h & 0xff;"),
+    ("bf16 subnormals decoded with 2^-134",
+     "v = ldexp((double)frac, -133);",
+     "v = ldexp((double)frac, -134);"),
+    ("bf16 operands: scales decoded as fp16",
+     "double s = decode(jb->dtype, jb->s[n * Kg + k / G]);",
+     "double s = qo_half_to_double(jb->s[n * Kg + k / G]);"),
+    ("bf16 operands: activations decoded as fp16",
+     "    decode_array(jb->dtype, jb->x, xd, M * K);\n    for (int64_t i = jb->n_begin; i < jb->n_end; ++i) {\n        const int64_t n = job_row(jb, i);\n        const uint32_t *row = jb->words + n * W;\n        for (int64_t k = 0; k < K; ++k) {",
+     "    decode_array(QO_F16, jb->x, xd, M * K);\n    for (int64_t i = jb->n_begin; i < jb->n_end; ++i) {\n        const int64_t n = job_row(jb, i);\n        const uint32_t *row = jb->words + n * W;\n        for (int64_t k = 0; k < K; ++k) {"),
     ("output row stride N instead of the list stride",
      "jb->y[m * jb->out_stride + i] = acc;\n            if (jb->absum)",
      "jb->y[m * jb->out_stride + (i + m) % jb->out_stride] = acc;\n            if (jb->absum)"),
