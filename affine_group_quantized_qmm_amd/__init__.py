@@ -172,8 +172,7 @@ def qmm_forward_rowexact(x, wq, scales, biases, bits: int, G: int, out=None) -> 
 
 
 def qmm_forward_bf16(x, wq, scales, biases, bits: int, G: int, out=None) -> torch.Tensor:
-    """The product with bfloat16 x, scales and biases (fp32 y); every row is
-    bitwise equal to the call on that row alone."""
+    """The product with bfloat16 x, scales and biases (fp32 y)."""
     M, K, N, dev = _operands(x, wq, scales, biases, bits, G, dtype=torch.bfloat16)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)

@@ -200,6 +200,7 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&
 // an integer below 2^8. Those pairs hold consecutive codes (2i, 2i + 1).
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 template <int P>
 __device__ __forceinline__ bf16x2_t code_pair4_bf16(uint32_t word)

@@ -85,7 +85,8 @@ bool mfma_supported(int bits, int G);  // whether launch_mfma handles (bits, G)
 // Register-resident multi-row kernel: whether it can run `a` (split included)
 // and its launcher (hipErrorInvalidValue when it cannot).
 bool mfma_xr_supported(const ProductArgs &a, int bits, int G);
-hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// bf16: x, scales and biases are bf16 bit patterns (single-projection launches only).
+hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream);
 // Tiled (MFMA-native) weight layout: whether the product on it supports
 // the shape (bits 2, 4, 8; K*bits a multiple of 512; K/G a multiple of 4;
 // parts that fit), the repack from the standard layout (N padded to whole

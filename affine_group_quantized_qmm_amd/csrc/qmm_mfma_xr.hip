@@ -136,9 +136,12 @@ __host__ __device__ constexpr int tiled_chunk_bytes() { return G * BITS / 32; }
 // TILED: weights in the tiled layout above (a.wq: codes, a.scales: the
 // (s, b) words); each lane loads its MFMA operands directly and nothing of
 // the weights goes through LDS.
-template <int BITS, int G, int XC, int SBW, int NST, bool FUSED, bool TILED = false>
+// BF16: x, scales and biases hold bf16 bit patterns; codes are widened to
+// bf16 and contracted with v_mfma_f32_16x16x32_bf16.
+template <int BITS, int G, int XC, int SBW, int NST, bool FUSED, bool TILED = false, bool BF16 = false>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
+    static_assert(!(TILED && BF16), "the tiled layout is fp16 only");
     using Geo = XrGeo<BITS, G, XC>;
     constexpr int CB = tiled_chunk_bytes<BITS, G>();       // tiled: bytes per lane chunk
     constexpr int NIT = (Geo::XG * CB + 15) / 16;          // tiled: 16-byte code loads per lane per tile
@@ -288,8 +291,10 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
             const int gg = min(pb + g, pe - 1);  // groups past the part re-read its last group
 #pragma unroll
             for (int h = 0; h < T; ++h)
-                xr[g][h] = to_pair_order<BITS>(
-                    *reinterpret_cast<const half8_t *>(xrow + (size_t)gg * G + c * CH + 8 * h));
+            {
+                const half8_t v = *reinterpret_cast<const half8_t *>(xrow + (size_t)gg * G + c * CH + 8 * h);
+                xr[g][h] = BF16 ? to_pair_order_bf16<BITS>(v) : to_pair_order<BITS>(v);
+            }
         }
     }
 
@@ -315,8 +320,15 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
 #pragma unroll
             for (int h = 0; h < T; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; e += 2)
-                    ps = __builtin_amdgcn_fdot2(half2_t{xr[g][h][e], xr[g][h][e + 1]}, one2, ps, false);
+                for (int e = 0; e < 8; e += 2) {
+                    const half2_t xe = {xr[g][h][e], xr[g][h][e + 1]};
+                    if constexpr (BF16) {
+                        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+                        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xe), ones, ps, false);
+                    } else {
+                        ps = __builtin_amdgcn_fdot2(xe, one2, ps, false);
+                    }
+                }
             xsl[(g * 4 + c) * 16 + i] = ps;
         }
 #pragma unroll
@@ -388,13 +400,25 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                                                            : (raw[w] >> chunk_shift);
                             }
                         }
-                        half2_t q[CH / 2];
-                        unpack_pairs<BITS, CH>(chunk, q);
+                        if constexpr (BF16) {
+                            bf16x2_t q[CH / 2];
+                            unpack_pairs_bf16<BITS, CH>(chunk, q);
 #pragma unroll
-                        for (int h = 0; h < T; ++h) {
-                            const half8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
-                                               q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
-                            P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[g][h], B, P[t], 0, 0, 0);
+                            for (int h = 0; h < T; ++h) {
+                                const bf16x8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
+                                                    q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
+                                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8_t, xr[g][h]), B, P[t], 0, 0, 0);
+                            }
+                        } else {
+                            half2_t q[CH / 2];
+                            unpack_pairs<BITS, CH>(chunk, q);
+#pragma unroll
+                            for (int h = 0; h < T; ++h) {
+                                const half8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
+                                                   q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
+                                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[g][h], B, P[t], 0, 0, 0);
+                            }
                         }
                     }
                 }
@@ -408,14 +432,21 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     sbo = sbrow[4 * u + c];
                     sbq = *reinterpret_cast<const u32x4 *>(sbrow + 4 * u);
                 }
-                const float so = half_bits_to_float((uint16_t)(sbo & 0xffffu));
-                const float bo = half_bits_to_float((uint16_t)(sbo >> 16)) - CodeOffset<BITS>::value * so;
+                float so, bo;
+                if constexpr (BF16) {
+                    so = bf16_bits_to_float(sbo & 0xffffu);
+                    bo = bf16_bits_to_float(sbo >> 16) - CodeOffsetBf16<BITS>::value * so;
+                } else {
+                    so = half_bits_to_float((uint16_t)(sbo & 0xffffu));
+                    bo = half_bits_to_float((uint16_t)(sbo >> 16)) - CodeOffset<BITS>::value * so;
+                }
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsa[u], bo, acc, 0, 0, 0);
                 // scale term: acc += s[n][g] * P_g
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     if (4 * u + t < XG) {
-                        const float sg = half_bits_to_float((uint16_t)(sbq[t] & 0xffffu));
+                        const float sg = BF16 ? bf16_bits_to_float(sbq[t] & 0xffffu)
+                                              : half_bits_to_float((uint16_t)(sbq[t] & 0xffffu));
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             acc[r] = __builtin_fmaf(sg, P[t][r], acc[r]);
@@ -518,7 +549,7 @@ int device_cu_count()
     return cached[dev];
 }
 
-template <int BITS, int G, int XC>
+template <int BITS, int G, int XC, bool BF16>
 hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
     XrArgs xa{a, plan.gran, (a.N + 15) / 16};
@@ -529,14 +560,17 @@ hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream
     const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
     const size_t lds = xr_lds_bytes<BITS, G, XC>(plan.KP);
     constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
+    // bf16 launches are single-projection only (no fused bf16 entry point)
+    const bool fused = !BF16 && a.nproj >= 2;
     // more than 64 KB of dynamic LDS must be allowed per kernel, once
     static bool allowed = false;
     if (!allowed) {
         const int cap = (int)xr_lds_bytes<BITS, G, XC>(kXrMaxParts);
-        const void *fns[4] = {reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false>),
-                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false>),
-                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, true>),
-                              reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, true>)};
+        const void *fns[4] = {
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>)};
         for (const void *f : fns) {
             const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
             if (e != hipSuccess)
@@ -544,17 +578,16 @@ hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream
         }
         allowed = true;
     }
-    const bool fused = a.nproj >= 2;
     if (plan.sbw == 4) {
         if (fused)
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, true>), grid, block, lds, stream, xa);
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>), grid, block, lds, stream, xa);
         else
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false>), grid, block, lds, stream, xa);
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>), grid, block, lds, stream, xa);
     } else {
         if (fused)
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, true>), grid, block, lds, stream, xa);
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>), grid, block, lds, stream, xa);
         else
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false>), grid, block, lds, stream, xa);
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>), grid, block, lds, stream, xa);
     }
     return hipGetLastError();
 }
@@ -580,7 +613,7 @@ bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
     return false;
 }
 
-template <int BITS, int G>
+template <int BITS, int G, bool BF16>
 hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
 {
     XrPlan plan;
@@ -589,9 +622,9 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
     if (!done)
         return hipSuccess;
     if (xc == xr_small_codes<BITS>())
-        return launch_xr_variant<BITS, G, xr_small_codes<BITS>()>(a, plan, stream);
+        return launch_xr_variant<BITS, G, xr_small_codes<BITS>(), BF16>(a, plan, stream);
     if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>())
-        return launch_xr_variant<BITS, G, xr_large_codes<BITS>()>(a, plan, stream);
+        return launch_xr_variant<BITS, G, xr_large_codes<BITS>(), BF16>(a, plan, stream);
     return hipErrorInvalidValue;
 }
 
@@ -774,12 +807,15 @@ bool mfma_xr_supported(const ProductArgs &a, int bits, int G)
     return false;
 }
 
-hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, hipStream_t stream)
+hipError_t launch_mfma_xr(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream)
 {
     bool done = false;
     hipError_t e = hipErrorInvalidValue;
+    if (bf16 && a.nproj >= 2)
+        return hipErrorInvalidValue;
 #define QMM_XR_CASE(B, GG) \
-    if (bits == B && G == GG) e = launch_xr_t<B, GG>(a, stream, done);
+    if (bits == B && G == GG) \
+        e = bf16 ? launch_xr_t<B, GG, true>(a, stream, done) : launch_xr_t<B, GG, false>(a, stream, done);
     QMM_XR_CASE(2, 32) QMM_XR_CASE(2, 64) QMM_XR_CASE(2, 128)
     QMM_XR_CASE(3, 32) QMM_XR_CASE(3, 64) QMM_XR_CASE(3, 128)
     QMM_XR_CASE(4, 32) QMM_XR_CASE(4, 64) QMM_XR_CASE(4, 128)

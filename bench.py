@@ -273,6 +273,13 @@ EXTRA_SHAPES = ((W.Shape("dense_up_5120x17408_w2g32", K=5120, N=17408, bits=2, G
                 *((sh, W.MIXED_M) for sh in W.MIXED))
 
 
+def kernel_label(qmm, M, shape, dtype):
+    """The kernel qmm_forward (or qmm_forward_bf16, which has no LDS-streaming
+    kernel and runs the VALU kernel instead) takes for M rows of `shape`."""
+    name = qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G)
+    return "qmv" if dtype == "bf16" and name == "mfma_lds" else name
+
+
 def measure_cells(qmm, shape, Ms, dev, stream, capture, dtype="f16"):
     """Per-M launch times of qmm_forward (qmm_forward_bf16 for dtype "bf16") on
     `shape` (rotated weight copies, graph replay)."""
@@ -306,8 +313,7 @@ def measure_cells(qmm, shape, Ms, dev, stream, capture, dtype="f16"):
         ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
         del g
         out[f"M{M}"] = {
-            "kernel": "qmv" if dtype == "bf16" else qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits,
-                                                                        shape.G),
+            "kernel": kernel_label(qmm, M, shape, dtype),
             "us_per_call": round(ms * 1e3, 3),
             "weight_GBps": round(shape.weight_bytes / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * shape.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),

@@ -138,13 +138,15 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
 /* bf16 variant (the pages' kernels take bf16 as well as fp16 activations
  * and scales: vmlx-swift pull request #565 page, the split-K verify commit's
  * fp16/bf16 tests and the bf16-activation affine mat-vec of the tiling-policy
- * commit). Same as qmm_forward_rowexact except that x [M,K], scales and
- * biases [N,K/G] hold bfloat16 bit patterns (uint16_t: the upper half of an
- * IEEE binary32); y is fp32. Codes are widened to exact bf16 integers and
- * dotted with the activations in fp32 (v_dot2_f32_bf16); every row of y is
- * bitwise equal to this function on that row alone. Runs the one-row VALU
- * kernel, up to 8 rows per launch (the weights are read once per 8 rows).
- * Same layout, alignment, ownership and error codes as qmm_forward. */
+ * commit). Same as qmm_forward except that x [M,K], scales and biases [N,K/G]
+ * hold bfloat16 bit patterns (uint16_t: the upper half of an IEEE binary32);
+ * y is fp32. Codes are widened to exact bf16 integers and contracted with the
+ * activations in fp32 (v_dot2_f32_bf16 on the one-row VALU kernel for one and
+ * two rows, v_mfma_f32_16x16x32_bf16 on the register-resident matrix-core
+ * kernel from three rows where it takes the shape, else the VALU kernel 8
+ * rows per launch). Results meet the same tolerance as qmm_forward; rows of
+ * a one- or two-row call are bitwise equal to one-row calls. Same layout,
+ * alignment, ownership and error codes as qmm_forward. */
 int qmm_forward_bf16(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
                      const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
                      hipStream_t stream);
