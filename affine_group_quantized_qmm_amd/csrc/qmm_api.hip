@@ -95,7 +95,7 @@ int launch_args(Kernel kind, const qmm::ProductArgs &full, int bits, int G, hipS
         switch (kind) {
         case Kernel::qmv: e = qmm::launch_qmv(a, bits, G, false, stream); break;
         case Kernel::mfma: e = qmm::launch_mfma_xr(a, bits, G, false, stream); break;
-        default: e = qmm::launch_mfma(a, bits, G, stream); break;
+        default: e = qmm::launch_mfma(a, bits, G, false, stream); break;
         }
         if (e != hipSuccess)
             return QMM_ERR_LAUNCH;
@@ -229,16 +229,15 @@ int qmm_forward_bf16(const uint16_t *x, const uint32_t *wq, const uint16_t *scal
     const int rc = qmm_validate(x, wq, scales, biases, y, M, K, N, bits, G, 0, nullptr, 0);
     if (rc != QMM_OK)
         return rc;
-    // the kernel choice of qmm_forward, without the LDS-streaming kernel
-    // (fp16 only): the VALU kernel for one and two rows and for shapes the
-    // register-resident kernel does not take
-    const bool mfma = M > kQmvMaxRows && xr_supported(K, N, bits, G, 1);
-    const int step = mfma ? kMaxRowsPerLaunch : kQmvRowsPerLaunch;
+    // qmm_forward's kernel choice
+    const Kernel kind = choose_kernel(M, K, N, bits, G, 1);
+    const int step = kind == Kernel::qmv ? kQmvRowsPerLaunch : kMaxRowsPerLaunch;
     const qmm::ProductArgs full = product_args(x, wq, scales, biases, y, M, K, N, 1);
     for (int m0 = 0; m0 < M; m0 += step) {
         const qmm::ProductArgs a = qmm::rows_of(full, m0, M - m0 < step ? M - m0 : step);
-        const hipError_t e = mfma ? qmm::launch_mfma_xr(a, bits, G, true, stream)
-                                  : qmm::launch_qmv(a, bits, G, true, stream);
+        const hipError_t e = kind == Kernel::qmv    ? qmm::launch_qmv(a, bits, G, true, stream)
+                             : kind == Kernel::mfma ? qmm::launch_mfma_xr(a, bits, G, true, stream)
+                                                    : qmm::launch_mfma(a, bits, G, true, stream);
         if (e != hipSuccess)
             return QMM_ERR_LAUNCH;
     }

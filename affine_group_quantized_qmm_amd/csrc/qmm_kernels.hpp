@@ -80,7 +80,8 @@ hipError_t launch_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int
                        hipStream_t stream);
 // bf16: x, scales and biases are bf16 bit patterns instead of fp16.
 hipError_t launch_qmv(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream);
-hipError_t launch_mfma(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// bf16: x, scales and biases are bf16 bit patterns (M >= 3 per launch).
+hipError_t launch_mfma(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream);
 bool mfma_supported(int bits, int G);  // whether launch_mfma handles (bits, G)
 // Register-resident multi-row kernel: whether it can run `a` (split included)
 // and its launcher (hipErrorInvalidValue when it cannot).

@@ -107,7 +107,9 @@ __device__ __forceinline__ void lds_barrier()
 #define QMM_MFMA_WAVES_PER_SIMD 4
 #endif
 
-template <int BITS, int G, int RT, int KP, int SPC, int PD, int MR>
+// BF16: x, scales and biases hold bf16 bit patterns; codes are widened to
+// bf16 and contracted with v_mfma_f32_16x16x32_bf16.
+template <int BITS, int G, int RT, int KP, int SPC, int PD, int MR, bool BF16>
 __global__ __launch_bounds__(RT *KP *kWave) __attribute__((amdgpu_waves_per_eu(QMM_MFMA_WAVES_PER_SIMD)))
 void mfma_kernel(const ProductArgs a)
 {
@@ -187,7 +189,8 @@ void mfma_kernel(const ProductArgs a)
                 const int m = rem / UPR, k = 8 * (rem % UPR);
                 const int gl = k / G, kg = k % G;
                 const int cb = kg / CH, h = (kg % CH) / 8;
-                xa[p][buf][((gl * T + h) * 4 + cb) * 16 + m] = to_pair_order<BITS>(xreg[t]);
+                xa[p][buf][((gl * T + h) * 4 + cb) * 16 + m] =
+                    BF16 ? to_pair_order_bf16<BITS>(xreg[t]) : to_pair_order<BITS>(xreg[t]);
             }
         }
     };
@@ -196,6 +199,10 @@ void mfma_kernel(const ProductArgs a)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         ones[e] = (_Float16)1.0f;
+    bf16x8_t ones_bf16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        ones_bf16[e] = (__bf16)1.0f;
 
     float acc[RLIVE];
 #pragma unroll
@@ -271,19 +278,39 @@ void mfma_kernel(const ProductArgs a)
 #pragma unroll
         for (int t = 0; t < SG; ++t) {
             if (g0 + t < pe) {  // wave-uniform
-                half2_t q[CH / 2];
-                unpack_pairs<BITS, CH>(chunk[t], q);
                 float4_t P = {0.f, 0.f, 0.f, 0.f}, XS = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BF16) {
+                    bf16x2_t q[CH / 2];
+                    unpack_pairs_bf16<BITS, CH>(chunk[t], q);
 #pragma unroll
-                for (int h = 0; h < T; ++h) {
-                    const half8_t A = xa[kp][buf][(((gl0 + t) * T + h) * 4 + c) * 16 + i];
-                    XS = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, XS, 0, 0, 0);
-                    const half8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
-                                       q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
-                    P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, P, 0, 0, 0);
+                    for (int h = 0; h < T; ++h) {
+                        const bf16x8_t A = __builtin_bit_cast(
+                            bf16x8_t, xa[kp][buf][(((gl0 + t) * T + h) * 4 + c) * 16 + i]);
+                        XS = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ones_bf16, XS, 0, 0, 0);
+                        const bf16x8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
+                                            q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
+                        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, P, 0, 0, 0);
+                    }
+                } else {
+                    half2_t q[CH / 2];
+                    unpack_pairs<BITS, CH>(chunk[t], q);
+#pragma unroll
+                    for (int h = 0; h < T; ++h) {
+                        const half8_t A = xa[kp][buf][(((gl0 + t) * T + h) * 4 + c) * 16 + i];
+                        XS = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, XS, 0, 0, 0);
+                        const half8_t B = {q[4 * h].x, q[4 * h].y, q[4 * h + 1].x, q[4 * h + 1].y,
+                                           q[4 * h + 2].x, q[4 * h + 2].y, q[4 * h + 3].x, q[4 * h + 3].y};
+                        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, P, 0, 0, 0);
+                    }
                 }
-                const float s = half_bits_to_float((uint16_t)(sb[t] & 0xffffu));
-                const float b = half_bits_to_float((uint16_t)(sb[t] >> 16)) - CodeOffset<BITS>::value * s;
+                float s, b;
+                if constexpr (BF16) {
+                    s = bf16_bits_to_float(sb[t] & 0xffffu);
+                    b = bf16_bits_to_float(sb[t] >> 16) - CodeOffsetBf16<BITS>::value * s;
+                } else {
+                    s = half_bits_to_float((uint16_t)(sb[t] & 0xffffu));
+                    b = half_bits_to_float((uint16_t)(sb[t] >> 16)) - CodeOffset<BITS>::value * s;
+                }
 #pragma unroll
                 for (int r = 0; r < RLIVE; ++r)
                     acc[r] += s * P[r] + b * XS[r];
@@ -362,25 +389,30 @@ constexpr int default_pd()
     return 2 * default_spc<BITS, G>() * (default_spc<BITS, G>() < 2 ? 2 : 1);
 }
 
-template <int BITS, int G, int MR, int RT = QMM_MFMA_RT, int KP = QMM_MFMA_KP, int SPC = default_spc<BITS, G>(),
-          int PD = default_pd<BITS, G>()>
+template <int BITS, int G, int MR, bool BF16, int RT = QMM_MFMA_RT, int KP = QMM_MFMA_KP,
+          int SPC = default_spc<BITS, G>(), int PD = default_pd<BITS, G>()>
 hipError_t launch_mfma_rows(const ProductArgs &a, hipStream_t stream)
 {
     static_assert(Geometry<BITS, G>::fits(), "lane chunk loads overrun the group");
     const int rows = 16 * RT;
     const dim3 grid((a.N + rows - 1) / rows, 1, a.split);
-    hipLaunchKernelGGL((mfma_kernel<BITS, G, RT, KP, SPC, PD, MR>), grid, dim3(RT * KP * kWave), 0, stream, a);
+    hipLaunchKernelGGL((mfma_kernel<BITS, G, RT, KP, SPC, PD, MR, BF16>), grid, dim3(RT * KP * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int BITS, int G>
-hipError_t launch_mfma_t(const ProductArgs &a, hipStream_t stream)
+hipError_t launch_mfma_t(const ProductArgs &a, bool bf16, hipStream_t stream)
 {
-    if (a.M <= 1) return launch_mfma_rows<BITS, G, 1>(a, stream);
-    if (a.M <= 2) return launch_mfma_rows<BITS, G, 2>(a, stream);
-    if (a.M <= 4) return launch_mfma_rows<BITS, G, 4>(a, stream);
-    if (a.M <= 8) return launch_mfma_rows<BITS, G, 8>(a, stream);
-    return launch_mfma_rows<BITS, G, 16>(a, stream);
+    if (bf16) {  // bf16 takes this kernel from three rows on only
+        if (a.M <= 4) return launch_mfma_rows<BITS, G, 4, true>(a, stream);
+        if (a.M <= 8) return launch_mfma_rows<BITS, G, 8, true>(a, stream);
+        return launch_mfma_rows<BITS, G, 16, true>(a, stream);
+    }
+    if (a.M <= 1) return launch_mfma_rows<BITS, G, 1, false>(a, stream);
+    if (a.M <= 2) return launch_mfma_rows<BITS, G, 2, false>(a, stream);
+    if (a.M <= 4) return launch_mfma_rows<BITS, G, 4, false>(a, stream);
+    if (a.M <= 8) return launch_mfma_rows<BITS, G, 8, false>(a, stream);
+    return launch_mfma_rows<BITS, G, 16, false>(a, stream);
 }
 
 }  // namespace
@@ -402,10 +434,10 @@ bool mfma_supported(int bits, int G)
     return false;
 }
 
-hipError_t launch_mfma(const ProductArgs &a, int bits, int G, hipStream_t stream)
+hipError_t launch_mfma(const ProductArgs &a, int bits, int G, bool bf16, hipStream_t stream)
 {
 #define QMM_MFMA_CASE(B, GG) \
-    if (bits == B && G == GG) return launch_mfma_t<B, GG>(a, stream);
+    if (bits == B && G == GG) return launch_mfma_t<B, GG>(a, bf16, stream);
     QMM_MFMA_CASE(2, 32) QMM_MFMA_CASE(2, 64) QMM_MFMA_CASE(2, 128)
     QMM_MFMA_CASE(3, 64) QMM_MFMA_CASE(3, 128)
     QMM_MFMA_CASE(4, 32) QMM_MFMA_CASE(4, 64) QMM_MFMA_CASE(4, 128)

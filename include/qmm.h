@@ -141,10 +141,9 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
  * commit). Same as qmm_forward except that x [M,K], scales and biases [N,K/G]
  * hold bfloat16 bit patterns (uint16_t: the upper half of an IEEE binary32);
  * y is fp32. Codes are widened to exact bf16 integers and contracted with the
- * activations in fp32 (v_dot2_f32_bf16 on the one-row VALU kernel for one and
- * two rows, v_mfma_f32_16x16x32_bf16 on the register-resident matrix-core
- * kernel from three rows where it takes the shape, else the VALU kernel 8
- * rows per launch). Results meet the same tolerance as qmm_forward; rows of
+ * activations in fp32 (v_dot2_f32_bf16 or v_mfma_f32_16x16x32_bf16), on the
+ * kernel qmm_forward takes for the same shape and row count (each kernel has
+ * a bf16 mode). Results meet the same tolerance as qmm_forward; rows of
  * a one- or two-row call are bitwise equal to one-row calls. Same layout,
  * alignment, ownership and error codes as qmm_forward. */
 int qmm_forward_bf16(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,

@@ -83,3 +83,24 @@ def test_bf16_rejects_fp16_tensors():
     dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=1, M=1, K=64, N=8, bits=4, G=32))
     with pytest.raises(TypeError):
         qmm.qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, 4, 32)
+
+
+@pytest.mark.parametrize("bits,G,K,M,kernel", [
+    (4, 32, 5120, 5, "mfma"),         # register-resident kernel
+    (4, 32, 17408, 5, "mfma_lds"),    # activations past the register-resident kernel: LDS-streaming kernel
+    (8, 64, 5120, 8, "mfma_lds"),
+    (3, 32, 17408, 16, "qmv"),        # neither matrix-core kernel: the VALU kernel
+    (6, 64, 5120, 16, "mfma"),
+])
+def test_bf16_each_kernel_path(bits, G, K, M, kernel):
+    """qmm_forward_bf16 takes qmm_forward's kernel; each kernel's bf16 mode
+    against the oracle (N = 97: ragged 16-row tiles)."""
+    N = 97
+    qmm = _gpu.lib()
+    assert qmm.qmm_kernel_name(M, K, N, bits, G) == kernel
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=990 + M + bits, M=M, K=K, N=N, bits=bits, G=G,
+                                                    dtype="bf16"))
+    y = qmm.qmm_forward_bf16(dp.x, dp.wq, dp.s, dp.b, bits, G)
+    torch.cuda.synchronize()
+    ref, absum = dp.oracle()
+    _gpu.assert_parity(y, ref, absum, f"bf16 {kernel} bits={bits} G={G} K={K} M={M}")
