@@ -13,8 +13,10 @@ value = weight bytes streamed per step / step time, where weight bytes per
 call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 
 Prints one JSON line. Synthetic data (seeded; no trained weights). Besides
-the headline cells the line carries `layer`: one decoder layer of the layer
-sweep at M = 1 and 8, its seven projections launched one by one and with
+the headline cells the line carries `layer_sweep`: the 64-layer sweep
+(13.63 GB of 4-bit weights resident in HBM, 448 projections per pass) at
+M = 1 and 8, one launch per projection and fused; `layer`: one decoder layer
+of the layer sweep at M = 1 and 8, its seven projections launched one by one and with
 q/k/v and gate/up fused (qmm_forward_fused); `other_workloads`: the
 dense up projection with 2- and 3-bit codes and the mixed 5/6/8-bit G=64
 projections, timed like the headline cells; and `tiled_layout`: the
@@ -411,6 +413,78 @@ def measure_layer(qmm, dev, stream, capture):
     return out
 
 
+def measure_sweep(qmm, dev, stream, capture, layers: int = W.SWEEP_LAYERS):
+    """The layer-stack sweep: `layers` dense decoder layers (q, k, v, o, gate,
+    up, down; 4-bit G=32; 13.63 GB of weights at 64 layers), all resident in
+    HBM, every projection once per pass, back to back on one stream at each
+    sweep M: 448 launches one per projection, and 256 with q/k/v and gate/up
+    fused. Layers are independent (each projection reads its own layer
+    input; no chaining). One pass is captured into a HIP graph and replayed.
+
+    The weights are drawn on the device with torch's generator (uniform
+    words, scales U(0.005, 0.02), biases U(-0.1, 0.1), x N(0, 1); seed
+    1000*layer + projection): drawing 13.6 GB on the host would take minutes.
+    Parity at these shapes is covered by the one-layer GPU tests."""
+    gen = torch.Generator(device=dev)
+    mats = []
+    for layer, j, sh, seed in W.sweep_shapes(layers):
+        gen.manual_seed(seed)
+        wq = torch.randint(-2 ** 31, 2 ** 31 - 1, (sh.N, sh.K * sh.bits // 32), dtype=torch.int32,
+                           device=dev, generator=gen)
+        lo, hi = qmm_inputs.SCALE_RANGE
+        s = (torch.rand((sh.N, sh.K // sh.G), device=dev, generator=gen) * (hi - lo) + lo).half()
+        lo, hi = qmm_inputs.BIAS_RANGE
+        b = (torch.rand((sh.N, sh.K // sh.G), device=dev, generator=gen) * (hi - lo) + lo).half()
+        mats.append((layer, j, sh, wq, s, b))
+    total = sum(sh.weight_bytes for _, _, sh, _, _, _ in mats)
+    names = [n for n, _, _ in W.LAYER_PROJECTIONS]
+    out = {"workload": (f"{layers} dense decoder layers (q, k, v, o, gate, up, down; 4-bit G=32), "
+                        f"{total / 1e9:.3f} GB of weights resident in HBM, one pass per step"),
+           "weight_bytes": total}
+    for M in W.SWEEP_M:
+        gen.manual_seed(7 + M)
+        # one input per layer input: q/k/v and gate/up share theirs (fused launches need it)
+        xin = {}
+        for layer in range(layers):
+            for key, K in (("qkv", 5120), ("o", 6144), ("gu", 5120), ("down", 17408)):
+                xin[layer, key] = torch.randn((M, K), device=dev, generator=gen).half()
+        key_of = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gu", "up": "gu", "down": "down"}
+        ys = {(layer, j): torch.empty((M, sh.N), dtype=torch.float32, device=dev)
+              for layer, j, sh, _, _, _ in mats}
+        by = {(layer, names[j]): (wq, s, b) for layer, j, _, wq, s, b in mats}
+
+        def separate(_i):
+            for layer, j, sh, wq, s, b in mats:
+                qmm.qmm_forward(xin[layer, key_of[names[j]]], wq, s, b, 4, 32, out=ys[layer, j])
+
+        def fused(_i):
+            for layer in range(layers):
+                qmm.qmm_forward_fused(xin[layer, "qkv"], [by[layer, "q"], by[layer, "k"], by[layer, "v"]], 4, 32,
+                                      outs=[ys[layer, 0], ys[layer, 1], ys[layer, 2]])
+                qmm.qmm_forward(xin[layer, "o"], *by[layer, "o"], 4, 32, out=ys[layer, 3])
+                qmm.qmm_forward_fused(xin[layer, "gu"], [by[layer, "gate"], by[layer, "up"]], 4, 32,
+                                      outs=[ys[layer, 4], ys[layer, 5]])
+                qmm.qmm_forward(xin[layer, "down"], *by[layer, "down"], 4, 32, out=ys[layer, 6])
+
+        cell = {}
+        for label, fn, launches in (("separate", separate, 7 * layers), ("fused", fused, 4 * layers)):
+            g = capture(fn, 1)
+            g.replay()
+            torch.cuda.synchronize()
+            times = [time_launches(lambda i, g=g: g.replay(), 1, stream) for _ in range(5)]
+            ms = sorted(times)[len(times) // 2]
+            del g
+            cell[f"{label}_launches"] = launches
+            cell[f"{label}_ms"] = round(ms, 3)
+            cell[f"{label}_weight_GBps"] = round(total / (ms * 1e-3) / 1e9, 1)
+            cell[f"{label}_pct_hbm_peak"] = round(100 * total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
+        out[f"M{M}"] = cell
+        del xin, ys
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
 PROFILE_REPS = 4
 
 
@@ -554,6 +628,7 @@ def main():
     }
     if not args.no_layer:
         out["layer"] = measure_layer(qmm, dev, stream, capture)
+        out["layer_sweep"] = measure_sweep(qmm, dev, stream, capture)
         out["other_workloads"] = {sh.name: measure_cells(qmm, sh, Ms, dev, stream, capture)
                                   for sh, Ms in EXTRA_SHAPES}
         out["tiled_layout"] = measure_tiled(qmm, shape, CELLS_M, dev, stream, capture)
