@@ -112,6 +112,25 @@ int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uin
 
 }  // namespace
 
+namespace qmm {
+
+int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace qmm
+
 extern "C" {
 
 const char *qmm_strerror(int code)

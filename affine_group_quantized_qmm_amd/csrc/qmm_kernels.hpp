@@ -74,6 +74,9 @@ inline ProductArgs rows_of(const ProductArgs &a, int m0, int count)
     return b;
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 // Each launcher returns a hipError_t from the launch (hipSuccess, or the
 // runtime's error) and hipErrorInvalidValue for an unsupported (bits, G).
 hipError_t launch_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,

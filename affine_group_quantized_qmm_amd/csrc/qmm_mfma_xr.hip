@@ -534,21 +534,6 @@ bool plan_xr(const ProductArgs &a, XrPlan &plan)
     return true;
 }
 
-int device_cu_count()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int BITS, int G, int XC, bool BF16>
 hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {

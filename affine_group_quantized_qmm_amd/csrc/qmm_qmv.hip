@@ -72,14 +72,15 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     __shared__ float xsum[MR][CHUNK_G];
     __shared__ uint32_t sbl[ROWS][CHUNK_G];   // (scale, bias) fp16 pair per row and group
 
-    static_assert(ROWS == 16, "a workgroup owns one 16-row tile");
-    const Slab slab = slab_of_tile(a, blockIdx.x);  // the projection of this workgroup's tile
+    static_assert(16 % ROWS == 0, "a workgroup owns a whole part of one 16-row tile");
+    constexpr int TPW = 16 / ROWS;                     // workgroups per 16-row tile
+    const Slab slab = slab_of_tile(a, blockIdx.x / TPW);  // the projection of this workgroup's tile
     const int K = a.K, N = slab.p.N, Kg = K / G;
     const size_t wpr = (size_t)K * BITS / 32;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int rho = lane / LPR, lam = lane % LPR;  // row within a row group, lane within the row
-    const int wg_row0 = slab.tile * ROWS;
+    const int wg_row0 = slab.tile * 16 + (int)(blockIdx.x % TPW) * ROWS;
     const int row0 = wg_row0 + wave * RPW;
 
     int gbeg = 0, gend = Kg;
@@ -319,20 +320,36 @@ int qmv_lanes_per_row(int slice)
     return slice <= max_slots1 * kWave && half % 2 == 1 ? 32 : 64;
 }
 
+// Rows per wave: four, or for projections of few rows one row group (RPI
+// rows: two with 32 lanes per row, one with 64), so that the launch has four
+// or two times more waves. A row's arithmetic depends on the lane map only,
+// so both give the same bits.
 template <int BITS, int G, int LPR, int MR, int S, bool BF16>
-hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
+hipError_t launch_qmv_upto(const ProductArgs &a, int slots, bool few_rows, hipStream_t stream)
 {
     // PD: with 32 lanes per row both row groups of a wave stay in flight
     // (measured: 12.7 us against 13.8 us with one on the 5120 x 17408 4-bit
     // projection at M = 1).
     constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
+    constexpr int RPI = kWave / LPR;
+    // the narrow variant is instantiated for the one- and two-row fp16 launches
+    constexpr bool NARROW = MR <= 2 && !BF16;
     if constexpr (S > 1) {
-        if (slots >= S)
-            return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR, BF16>(a, stream);
-        return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, stream);
-    } else {
-        return launch_qmv_slots<BITS, G, LPR, 1, kRowsPerWave, PDR, MR, BF16>(a, stream);
+        if (slots < S)
+            return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, few_rows, stream);
     }
+    if constexpr (NARROW) {
+        if (few_rows)
+            return launch_qmv_slots<BITS, G, LPR, S, RPI, PDR, MR, BF16>(a, stream);
+    }
+    return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR, BF16>(a, stream);
+}
+
+// Projections of fewer 16-row tiles than two per compute unit take the
+// narrow variant (a fused launch counts all its projections' tiles).
+inline bool qmv_few_rows(const ProductArgs &a)
+{
+    return (a.N + 15) / 16 < 2 * device_cu_count();
 }
 
 template <int BITS, int G, int MR, bool BF16>
@@ -345,11 +362,13 @@ hipError_t launch_qmv_rows(const ProductArgs &a, hipStream_t stream)
     if (lpr == 32) {
         constexpr int max_s = chunk_limit(MR) / (MR * 32 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8), BF16>(a, need, stream);
+            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8), BF16>(a, need, qmv_few_rows(a),
+                                                                                   stream);
     } else {
         constexpr int max_s = chunk_limit(MR) / (MR * 64 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4), BF16>(a, need, stream);
+            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4), BF16>(a, need, qmv_few_rows(a),
+                                                                                   stream);
     }
     return hipErrorInvalidValue;
 }
