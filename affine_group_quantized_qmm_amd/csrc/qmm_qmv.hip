@@ -320,36 +320,26 @@ int qmv_lanes_per_row(int slice)
     return slice <= max_slots1 * kWave && half % 2 == 1 ? 32 : 64;
 }
 
-// Rows per wave: four, or for projections of few rows one row group (RPI
-// rows: two with 32 lanes per row, one with 64), so that the launch has four
-// or two times more waves. A row's arithmetic depends on the lane map only,
-// so both give the same bits.
+// Rows per wave: one row group (RPI rows: two with 32 lanes per row, one
+// with 64) for the one- and two-row fp16 launches, four otherwise. The
+// narrow form has two or four times more waves, each with a shorter chain
+// of tasks: 12.0-12.7 us against 12.7-13.1 us on the 5120 x 17408 4-bit
+// projection at M = 1, 9.4 against 11.2 us on a 5120 x 5120 5-bit one (320
+// tiles: 1.25 waves per SIMD in the wide form). A row's arithmetic depends
+// on the lane map only, so both forms give the same bits.
 template <int BITS, int G, int LPR, int MR, int S, bool BF16>
-hipError_t launch_qmv_upto(const ProductArgs &a, int slots, bool few_rows, hipStream_t stream)
+hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
 {
     // PD: with 32 lanes per row both row groups of a wave stay in flight
     // (measured: 12.7 us against 13.8 us with one on the 5120 x 17408 4-bit
     // projection at M = 1).
     constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
-    constexpr int RPI = kWave / LPR;
-    // the narrow variant is instantiated for the one- and two-row fp16 launches
-    constexpr bool NARROW = MR <= 2 && !BF16;
+    constexpr int RPW = MR <= 2 && !BF16 ? kWave / LPR : kRowsPerWave;
     if constexpr (S > 1) {
         if (slots < S)
-            return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, few_rows, stream);
+            return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, stream);
     }
-    if constexpr (NARROW) {
-        if (few_rows)
-            return launch_qmv_slots<BITS, G, LPR, S, RPI, PDR, MR, BF16>(a, stream);
-    }
-    return launch_qmv_slots<BITS, G, LPR, S, kRowsPerWave, PDR, MR, BF16>(a, stream);
-}
-
-// Projections of fewer 16-row tiles than two per compute unit take the
-// narrow variant (a fused launch counts all its projections' tiles).
-inline bool qmv_few_rows(const ProductArgs &a)
-{
-    return (a.N + 15) / 16 < 2 * device_cu_count();
+    return launch_qmv_slots<BITS, G, LPR, S, RPW, PDR, MR, BF16>(a, stream);
 }
 
 template <int BITS, int G, int MR, bool BF16>
@@ -362,13 +352,11 @@ hipError_t launch_qmv_rows(const ProductArgs &a, hipStream_t stream)
     if (lpr == 32) {
         constexpr int max_s = chunk_limit(MR) / (MR * 32 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8), BF16>(a, need, qmv_few_rows(a),
-                                                                                   stream);
+            return launch_qmv_upto<BITS, G, 32, MR, (max_s < 8 ? max_s : 8), BF16>(a, need, stream);
     } else {
         constexpr int max_s = chunk_limit(MR) / (MR * 64 * G);
         if constexpr (max_s >= 1)
-            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4), BF16>(a, need, qmv_few_rows(a),
-                                                                                   stream);
+            return launch_qmv_upto<BITS, G, 64, MR, (max_s < 4 ? max_s : 4), BF16>(a, need, stream);
     }
     return hipErrorInvalidValue;
 }
