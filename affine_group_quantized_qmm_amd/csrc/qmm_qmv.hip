@@ -321,7 +321,7 @@ int qmv_lanes_per_row(int slice)
 }
 
 // Rows per wave: one row group (RPI rows: two with 32 lanes per row, one
-// with 64) for the one- and two-row fp16 launches, four otherwise. The
+// with 64) for the one- and two-row launches, four otherwise. The
 // narrow form has two or four times more waves, each with a shorter chain
 // of tasks: 12.0-12.7 us against 12.7-13.1 us on the 5120 x 17408 4-bit
 // projection at M = 1, 9.4 against 11.2 us on a 5120 x 5120 5-bit one (320
@@ -334,7 +334,7 @@ hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
     // (measured: 12.7 us against 13.8 us with one on the 5120 x 17408 4-bit
     // projection at M = 1).
     constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
-    constexpr int RPW = MR <= 2 && !BF16 ? kWave / LPR : kRowsPerWave;
+    constexpr int RPW = MR <= 2 ? kWave / LPR : kRowsPerWave;
     if constexpr (S > 1) {
         if (slots < S)
             return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, stream);
