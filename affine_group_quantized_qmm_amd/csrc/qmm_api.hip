@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 namespace {
 
 constexpr int kMaxRowsPerLaunch = 16;  // rows of one multi-row launch (one MFMA tile)
@@ -116,17 +118,17 @@ namespace qmm {
 
 int device_cu_count()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];  // zero until queried; racing queries store the same value
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 }  // namespace qmm

@@ -30,6 +30,8 @@
 // scales and biases go the same way, interleaved as (s | b << 16) words. The
 // loads of the tile NST ahead are issued as soon as the current one is in
 // LDS, so they stream while NST tiles are computed.
+#include <atomic>
+
 #include "qmm_device.hpp"
 #include "qmm_kernels.hpp"
 
@@ -498,6 +500,26 @@ struct XrPlan {
     int KP, gran, sbw;
 };
 
+// More than 64 KB of dynamic LDS must be allowed per kernel: set the limit
+// of `fns` once per device (bit d of `done` records device d; two threads
+// racing both set it, which is harmless).
+hipError_t allow_dynamic_lds(const void *const *fns, int count, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = 0;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit)
+        return hipSuccess;
+    for (int k = 0; k < count; ++k) {
+        const hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess)
+            return e;
+    }
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
 // The register-resident kernel needs: whole 16-byte rows of packed codes,
 // K slices starting on a granule, at most kXrMaxParts parts of at most
 // XC activations each, and no empty part.
@@ -548,20 +570,17 @@ hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream
     // bf16 launches are single-projection only (no fused bf16 entry point)
     const bool fused = !BF16 && a.nproj >= 2;
     // more than 64 KB of dynamic LDS must be allowed per kernel, once
-    static bool allowed = false;
-    if (!allowed) {
+    static std::atomic<uint64_t> allowed{0};
+    {
         const int cap = (int)xr_lds_bytes<BITS, G, XC>(kXrMaxParts);
         const void *fns[4] = {
             reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>),
             reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>),
             reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>),
             reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>)};
-        for (const void *f : fns) {
-            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-            if (e != hipSuccess)
-                return e;
-        }
-        allowed = true;
+        const hipError_t e = allow_dynamic_lds(fns, 4, cap, allowed);
+        if (e != hipSuccess)
+            return e;
     }
     if (plan.sbw == 4) {
         if (fused)
@@ -736,14 +755,12 @@ hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hip
     const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
     const size_t lds = xr_lds_bytes<BITS, G, XC, true>(plan.KP);
     constexpr int NST = xr_tiled_stages<BITS, G, XC>();
-    static bool allowed = false;
-    if (!allowed) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)xr_lds_bytes<BITS, G, XC, true>(kXrMaxParts));
+    static std::atomic<uint64_t> allowed{0};
+    {
+        const void *fns[1] = {reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>)};
+        const hipError_t e = allow_dynamic_lds(fns, 1, (int)xr_lds_bytes<BITS, G, XC, true>(kXrMaxParts), allowed);
         if (e != hipSuccess)
             return e;
-        allowed = true;
     }
     hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>), dim3(gx), dim3(plan.KP * kWave), lds,
                        stream, xa);
