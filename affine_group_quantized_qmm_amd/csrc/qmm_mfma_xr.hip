@@ -597,11 +597,18 @@ hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream
 }
 
 // Variants of a width, preferred first: fewer activation registers leave
-// room for more tiles in flight; the longer parts take longer K.
+// room for more tiles in flight; the longer parts take longer K. 8-bit codes
+// take 640-activation parts (their 40 registers of weight loads per tile
+// leave no room for 768); the tiled layout keeps 512 for them (its loads
+// stay in registers through the computation).
 template <int BITS>
-constexpr int xr_small_codes() { return BITS == 8 ? 512 : 640; }
+constexpr int xr_small_codes() { return 640; }
 template <int BITS>
-constexpr int xr_large_codes() { return BITS == 8 ? 512 : 768; }
+constexpr int xr_large_codes() { return BITS == 8 ? 640 : 768; }
+template <int BITS>
+constexpr int xr_tiled_small_codes() { return BITS == 8 ? 512 : 640; }
+template <int BITS>
+constexpr int xr_tiled_large_codes() { return BITS == 8 ? 512 : 768; }
 
 template <int BITS, int G>
 bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
@@ -772,11 +779,11 @@ hipError_t launch_xr_tiled_t(const ProductArgs &a, hipStream_t stream, bool &don
 {
     XrPlan plan;
     done = true;
-    if (plan_xr_tiled<BITS, G, xr_small_codes<BITS>()>(a, plan))
-        return launch_xr_tiled_variant<BITS, G, xr_small_codes<BITS>()>(a, plan, stream);
-    if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>()) {
-        if (plan_xr_tiled<BITS, G, xr_large_codes<BITS>()>(a, plan))
-            return launch_xr_tiled_variant<BITS, G, xr_large_codes<BITS>()>(a, plan, stream);
+    if (plan_xr_tiled<BITS, G, xr_tiled_small_codes<BITS>()>(a, plan))
+        return launch_xr_tiled_variant<BITS, G, xr_tiled_small_codes<BITS>()>(a, plan, stream);
+    if constexpr (xr_tiled_large_codes<BITS>() != xr_tiled_small_codes<BITS>()) {
+        if (plan_xr_tiled<BITS, G, xr_tiled_large_codes<BITS>()>(a, plan))
+            return launch_xr_tiled_variant<BITS, G, xr_tiled_large_codes<BITS>()>(a, plan, stream);
     }
     done = false;
     return hipSuccess;
@@ -786,9 +793,9 @@ template <int BITS, int G>
 bool tiled_supported_t(const ProductArgs &a)
 {
     XrPlan plan;
-    if (plan_xr_tiled<BITS, G, xr_small_codes<BITS>()>(a, plan))
+    if (plan_xr_tiled<BITS, G, xr_tiled_small_codes<BITS>()>(a, plan))
         return true;
-    return plan_xr_tiled<BITS, G, xr_large_codes<BITS>()>(a, plan);
+    return plan_xr_tiled<BITS, G, xr_tiled_large_codes<BITS>()>(a, plan);
 }
 
 }  // namespace

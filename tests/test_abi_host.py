@@ -89,7 +89,8 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma_lds"
     # 5-bit rows of 13 groups are not whole 16-byte units
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
-    assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma"      # 8-bit: parts of 640 activations
+    assert qmm.qmm_kernel_name(4, 17408, 5120, 8, 64) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 6, 64) == "mfma"
     # 2- and 3-bit codes
     assert qmm.qmm_kernel_name(2, 5120, 1000, 2, 32) == "qmv"

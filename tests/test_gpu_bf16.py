@@ -88,7 +88,8 @@ def test_bf16_rejects_fp16_tensors():
 @pytest.mark.parametrize("bits,G,K,M,kernel", [
     (4, 32, 5120, 5, "mfma"),         # register-resident kernel
     (4, 32, 17408, 5, "mfma_lds"),    # activations past the register-resident kernel: LDS-streaming kernel
-    (8, 64, 5120, 8, "mfma_lds"),
+    (8, 64, 5120, 8, "mfma"),
+    (8, 64, 17408, 8, "mfma_lds"),
     (3, 32, 17408, 16, "qmv"),        # neither matrix-core kernel: the VALU kernel
     (6, 64, 5120, 16, "mfma"),
 ])
