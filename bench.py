@@ -15,7 +15,9 @@ call = N*K*(bits/8 + 4/G) (codes plus fp16 scale and bias per group).
 Prints one JSON line. Synthetic data (seeded; no trained weights). Besides
 the headline cells the line carries `layer_sweep`: the 64-layer sweep
 (13.63 GB of 4-bit weights resident in HBM, 448 projections per pass) at
-M = 1 and 8, one launch per projection and fused; `layer`: one decoder layer
+M = 1 and 8, one launch per projection and fused; `long_k`: the 17408 x 5120
+down projection at M = 16 through qmm_forward_splitk, S = 1, 2, 4, 8;
+`layer`: one decoder layer
 of the layer sweep at M = 1 and 8, its seven projections launched one by one and with
 q/k/v and gate/up fused (qmm_forward_fused); `other_workloads`: the
 dense up projection with 2- and 3-bit codes and the mixed 5/6/8-bit G=64
@@ -413,12 +415,53 @@ def measure_layer(qmm, dev, stream, capture):
     return out
 
 
+def measure_long_k(qmm, dev, stream, capture):
+    """The long-K down projection (K = 17408, N = 5120, 4-bit G=32) at M = 16
+    through qmm_forward_splitk at each split factor (S = 1 is one launch
+    without a workspace; S > 1 writes S fp32 partials and sums them in a
+    second launch), weight copies rotated as in the headline cells."""
+    shape, M = W.LONG_K, W.LONG_K_M
+    p = qmm_inputs.make_problem(seed=11, M=M, K=shape.K, N=shape.N, bits=shape.bits, G=shape.G,
+                                packed_words=True)
+    wq = torch.from_numpy(p.words.view(np.int32)).to(dev)
+    s = torch.from_numpy(p.scales).to(dev)
+    b = torch.from_numpy(p.biases).to(dev)
+    copies = max(2, -(-ROTATION_BYTES // shape.weight_bytes))
+    sets = [(wq, s, b)] + [(wq.clone(), s.clone(), b.clone()) for _ in range(copies - 1)]
+    x = torch.from_numpy(p.x).to(dev)
+    y = torch.empty((M, shape.N), dtype=torch.float32, device=dev)
+    out = {"workload": f"{shape.name} at M = {M}, qmm_forward_splitk", "weight_bytes_per_call": shape.weight_bytes,
+           "weight_copies_rotated": copies}
+    for S in W.LONG_K_SPLITS:
+        need = qmm.qmm_splitk_workspace_bytes(M, shape.N, S)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+
+        def call(i, S=S, ws=ws):
+            qmm.qmm_forward_splitk(x, *sets[i % copies], shape.bits, shape.G, S, workspace=ws, out=y)
+
+        reps = max(50, 2 * copies)
+        g = capture(call, reps)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_launches(lambda i, g=g: g.replay(), 1, stream) / reps
+        del g
+        out[f"S{S}"] = {
+            "kernel": qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G) if S == 1 else "split",
+            "us_per_call": round(ms * 1e3, 3),
+            "weight_GBps": round(shape.weight_bytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * shape.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "partial_bytes": 8 * S * M * shape.N if S > 1 else 0,
+        }
+    return out
+
+
 def measure_sweep(qmm, dev, stream, capture, layers: int = W.SWEEP_LAYERS):
     """The layer-stack sweep: `layers` dense decoder layers (q, k, v, o, gate,
     up, down; 4-bit G=32; 13.63 GB of weights at 64 layers), all resident in
     HBM, every projection once per pass, back to back on one stream at each
-    sweep M: 448 launches one per projection, and 256 with q/k/v and gate/up
-    fused. Layers are independent (each projection reads its own layer
+    sweep M: 448 launches one per projection, 256 with q/k/v and gate/up
+    fused, and 320 with the down projection through split-K (S = 4: a slice
+    launch and the in-order reduction). Layers are independent (each projection reads its own layer
     input; no chaining). One pass is captured into a HIP graph and replayed.
 
     The weights are drawn on the device with torch's generator (uniform
@@ -466,8 +509,22 @@ def measure_sweep(qmm, dev, stream, capture, layers: int = W.SWEEP_LAYERS):
                                       outs=[ys[layer, 4], ys[layer, 5]])
                 qmm.qmm_forward(xin[layer, "down"], *by[layer, "down"], 4, 32, out=ys[layer, 6])
 
+        # the down projection (K = 17408) through split-K, S = 4, as a caller would run it
+        ws = torch.empty(qmm.qmm_splitk_workspace_bytes(M, 5120, 4) // 4, dtype=torch.float32, device=dev)
+
+        def fused_splitk(_i):
+            for layer in range(layers):
+                qmm.qmm_forward_fused(xin[layer, "qkv"], [by[layer, "q"], by[layer, "k"], by[layer, "v"]], 4, 32,
+                                      outs=[ys[layer, 0], ys[layer, 1], ys[layer, 2]])
+                qmm.qmm_forward(xin[layer, "o"], *by[layer, "o"], 4, 32, out=ys[layer, 3])
+                qmm.qmm_forward_fused(xin[layer, "gu"], [by[layer, "gate"], by[layer, "up"]], 4, 32,
+                                      outs=[ys[layer, 4], ys[layer, 5]])
+                qmm.qmm_forward_splitk(xin[layer, "down"], *by[layer, "down"], 4, 32, 4, workspace=ws,
+                                       out=ys[layer, 6])
+
         cell = {}
-        for label, fn, launches in (("separate", separate, 7 * layers), ("fused", fused, 4 * layers)):
+        for label, fn, launches in (("separate", separate, 7 * layers), ("fused", fused, 4 * layers),
+                                    ("fused_splitk_down", fused_splitk, 5 * layers)):
             g = capture(fn, 1)
             g.replay()
             torch.cuda.synchronize()
@@ -629,6 +686,7 @@ def main():
     if not args.no_layer:
         out["layer"] = measure_layer(qmm, dev, stream, capture)
         out["layer_sweep"] = measure_sweep(qmm, dev, stream, capture)
+        out["long_k"] = measure_long_k(qmm, dev, stream, capture)
         out["other_workloads"] = {sh.name: measure_cells(qmm, sh, Ms, dev, stream, capture)
                                   for sh, Ms in EXTRA_SHAPES}
         out["tiled_layout"] = measure_tiled(qmm, shape, CELLS_M, dev, stream, capture)
