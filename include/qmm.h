@@ -91,10 +91,11 @@ int qmm_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,
  * x [M,K] fp16, wq [N, K*bits/32] uint32, scales/biases [N, K/G] fp16,
  * y [M,N] fp32; all device pointers, 16-byte aligned.
  * The kernel is chosen on the host from (M, bits, G, K, N): a
- * one-row mat-vec for M = 1 and a multi-row kernel that streams the
- * weights once for all rows otherwise (the vmlx-swift pull request #565
- * page, tiling-policy commit, routes fewer than four rows to the
- * one-row mat-vec because it is faster there).
+ * mat-vec kernel for one and two rows and a multi-row matrix-core kernel
+ * that streams the weights once for all rows otherwise (the vmlx-swift pull
+ * request #565 page, tiling-policy commit, routes fewer than four rows to
+ * the one-row mat-vec because it is faster there; here the matrix cores win
+ * from three rows on).
  */
 int qmm_forward(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
                 const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
