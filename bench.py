@@ -272,16 +272,16 @@ def cpu_baseline(p, shape, rows: int, min_seconds: float = 10.0):
 # Other workloads, timed like the headline cells (not part of `value`):
 # the dense up projection with 2- and 3-bit codes, and the mixed 5/6/8-bit
 # G=64 projections.
-EXTRA_SHAPES = ((W.Shape("dense_up_5120x17408_w2g32", K=5120, N=17408, bits=2, G=32), (1, 16)),
+# the headline projection at the verify widths outside the headline cells, then other widths
+EXTRA_SHAPES = ((W.DENSE_UP, tuple(m for m in W.DENSE_UP_M if m not in CELLS_M)),
+                (W.Shape("dense_up_5120x17408_w2g32", K=5120, N=17408, bits=2, G=32), (1, 16)),
                 (W.Shape("dense_up_5120x17408_w3g32", K=5120, N=17408, bits=3, G=32), (1, 16)),
                 *((sh, W.MIXED_M) for sh in W.MIXED))
 
 
 def kernel_label(qmm, M, shape, dtype):
-    """The kernel qmm_forward (or qmm_forward_bf16, which has no LDS-streaming
-    kernel and runs the VALU kernel instead) takes for M rows of `shape`."""
-    name = qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G)
-    return "qmv" if dtype == "bf16" and name == "mfma_lds" else name
+    """The kernel qmm_forward (or qmm_forward_bf16) takes for M rows of `shape`."""
+    return qmm.qmm_kernel_name(M, shape.K, shape.N, shape.bits, shape.G)
 
 
 def measure_cells(qmm, shape, Ms, dev, stream, capture, dtype="f16"):
