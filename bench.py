@@ -121,6 +121,15 @@ def _per_dispatch(rows, counter):
     return [(d, acc[d][0], acc[d][1]) for d in sorted(acc)]
 
 
+def _repo_relative(path: str) -> str:
+    """`path` relative to the repository root when it lies inside it."""
+    p = Path(path).resolve()
+    try:
+        return str(p.relative_to(ROOT))
+    except ValueError:
+        return str(path)
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, out: str):
     """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the profile run -> text summary."""
     fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
@@ -155,7 +164,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str):
         "# commands (from the repository root on the GPU host):",
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o run -- python3 bench.py --profile-run",
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o run -- python3 bench.py --profile-run",
-        f"#   python3 bench.py --summarize-pmc <F> <W> {Path(out).relative_to(ROOT) if Path(out).is_absolute() else out}",
+        f"#   python3 bench.py --summarize-pmc <F> <W> {_repo_relative(out)}",
         f"copy_calibration kernel={f_copy[0][0].split('(')[0][:60].replace(' ', '_')} "
         f"bytes={copy_bytes} fetch_kib={f_copy_kib:.1f} write_kib={w_copy_kib:.1f} "
         f"fetch_scale={f_scale:.4f} write_scale={w_scale:.4f}",
