@@ -87,6 +87,7 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 6144, 1024, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 65536, 64, 4, 32) == "mfma_lds"
     # 5-bit rows of 13 groups are not whole 16-byte units
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma"      # 8-bit: parts of 640 activations
@@ -100,6 +101,7 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(8, 17408, 1000, 2, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 64) == "mfma_lds"
     assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 32) == "qmv"
+    assert qmm.qmm_kernel_name(8, 65536, 1000, 3, 32) == "qmv"
 
 
 def test_fused_rejects_before_launch():

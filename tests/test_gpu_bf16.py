@@ -90,7 +90,10 @@ def test_bf16_rejects_fp16_tensors():
     (4, 32, 17408, 5, "mfma_lds"),    # activations past the register-resident kernel: LDS-streaming kernel
     (8, 64, 5120, 8, "mfma"),
     (8, 64, 17408, 8, "mfma_lds"),
+    (5, 32, 13 * 32, 4, "mfma_lds"),  # rows not whole 16-byte units
+    (4, 32, 65536, 3, "mfma_lds"),
     (3, 32, 17408, 16, "qmv"),        # neither matrix-core kernel: the VALU kernel
+    (3, 32, 65536, 3, "qmv"),
     (6, 64, 5120, 16, "mfma"),
 ])
 def test_bf16_each_kernel_path(bits, G, K, M, kernel):
