@@ -63,3 +63,12 @@ def test_traffic_dropped_when_the_kernel_changed(tmp_path, monkeypatch):
     assert bench.read_traffic("qmv", [1]) is None      # stale fingerprint
     assert bench.read_traffic("mfma", [4]) == 456.0
     assert bench.read_traffic("mfma", [4, 16]) is None  # a cell missing
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    """bench.py measures one GPU: --gpus N with N != 1 exits before any GPU work."""
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU only" in capsys.readouterr().err
