@@ -29,6 +29,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions (compiler-generated v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS regions are written and read through different types (staged words,
+    # group sums, (scale, bias) words): no type-based alias assumptions
+    "-fno-strict-aliasing",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]

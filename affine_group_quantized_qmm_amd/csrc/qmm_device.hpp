@@ -127,17 +127,19 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t m
     return r;
 }
 
-// 4-bit codes take a cheaper route: all codes of a word are moved to bits
-// 4..7 of their half (the high nibble of each byte pair needs no shift, the
-// others one shift each) and become 64 + code with one v_and_or_b32. The
-// constant 64 is not subtracted per code: since every code carries it,
-// sum_k (64 + q_k) x_k = P + 64 XS, and the epilogue folds 64*s*XS into the
-// bias (b' = b - 64 s). Three shifts and four v_and_or_b32 per word.
+// 4-bit codes take a cheaper route that needs no exponent at all: a 16-bit
+// half whose exponent field is zero is the fp16 subnormal (fraction) * 2^-24,
+// so a code moved to bits 4..7 of its half, with every other bit cleared,
+// is exactly q * 2^-20. Each pair costs one shift (none for P = 1) and one
+// mask: three shifts and four ands per word, and no constant to remove
+// afterwards. The matrix cores and v_dot2 multiply fp16 subnormals exactly
+// (no flush to zero on gfx950), so the group dot product comes out as
+// 2^-20 * P; the epilogue multiplies by CodeScale<4>::value = 2^20 (a power of
+// two, so no rounding is added).
 template <int P>
-__device__ __forceinline__ half2_t code_pair4_offset64(uint32_t word)
+__device__ __forceinline__ half2_t code_pair4(uint32_t word)
 {
     constexpr uint32_t mask = 0x00F000F0u;          // bits 4..7 of each half
-    constexpr uint32_t magic = 0x54005400u;         // 2^6 in each half
     uint32_t v;
     if constexpr (P == 0)
         v = word << 4;
@@ -147,8 +149,34 @@ __device__ __forceinline__ half2_t code_pair4_offset64(uint32_t word)
         v = word >> 4;
     else
         v = word >> 8;
-    return __builtin_bit_cast(half2_t, and_or(v, mask, magic));
+    return __builtin_bit_cast(half2_t, v & mask);
 }
+
+// The subnormal form suits the matrix cores only. v_dot2_f32_f16 accumulates
+// products of subnormal operands with reduced precision (tens of ulps on
+// gfx950, measured), so the v_dot2 kernels widen 4-bit codes to normal fp16
+// integers instead: pairs 0 and 2 of a word (bits 0..3 of each half, from
+// the word and the word shifted by 8) become 1024 + q under the exponent of
+// 2^10, pairs 1 and 3 (bits 4..7) become 64 + q under 2^6, and one packed
+// subtract removes the constant exactly. One shift, four v_and_or_b32 and
+// four v_pk_add_f16 per word; the codes come out as exact integers (scale 1).
+template <int P>
+__device__ __forceinline__ half2_t code_pair4_int(uint32_t word, uint32_t word_hi)
+{
+    constexpr bool low = P % 2 == 0;
+    constexpr uint32_t mask = low ? 0x000F000Fu : 0x00F000F0u;
+    constexpr uint32_t magic = low ? 0x64006400u : 0x54005400u;  // 2^10 or 2^6 in each half
+    const half2_t v = __builtin_bit_cast(half2_t, and_or(P < 2 ? word : word_hi, mask, magic));
+    const _Float16 off = low ? (_Float16)1024.0f : (_Float16)64.0f;
+    return v - half2_t{off, off};
+}
+
+// Factor that turns a widened-code dot product into the true one.
+template <int BITS>
+struct CodeScale {
+    static constexpr float value = BITS == 4 ? 1048576.0f : 1.0f;          // 2^20
+    static constexpr float inverse = BITS == 4 ? 1.0f / 1048576.0f : 1.0f; // 2^-20
+};
 
 // The 8 activations of one MFMA K-block (8 consecutive codes of a lane's
 // chunk) rearranged into the pair order of unpack_pairs.
@@ -161,25 +189,34 @@ __device__ __forceinline__ half8_t to_pair_order(half8_t v)
         return __builtin_shufflevector(v, v, 0, 2, 1, 3, 4, 6, 5, 7);
 }
 
-// Offset every widened code carries (see code_pair4_offset64): the epilogue
-// uses s * (P' - kCodeOffset * XS) = s * P.
-template <int BITS>
-struct CodeOffset {
-    static constexpr float value = BITS == 4 ? 64.0f : 0.0f;
-};
-
 template <int BITS, int NW, int... Ps>
 __device__ __forceinline__ void unpack_pairs_impl(const uint32_t (&w)[NW], half2_t *out,
                                                   std::integer_sequence<int, Ps...>)
 {
     if constexpr (BITS == 4)
-        ((out[Ps] = code_pair4_offset64<Ps % 4>(w[Ps / 4])), ...);
+        ((out[Ps] = code_pair4<Ps % 4>(w[Ps / 4])), ...);
     else
         ((out[Ps] = code_pair<BITS, Ps>(w)), ...);
 }
 
+// 4-bit codes as exact fp16 integers for v_dot2 (code_pair4_int): pair P of
+// word j is out[4j + P], in the pair order of unpack_pairs.
+template <int NCODES, int NW>
+__device__ __forceinline__ void unpack_pairs4_int(const uint32_t (&w)[NW], half2_t (&out)[NCODES / 2])
+{
+    static_assert(NCODES == 8 * NW, "one word per 8 codes");
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        const uint32_t hi = w[j] >> 8;
+        out[4 * j + 0] = code_pair4_int<0>(w[j], hi);
+        out[4 * j + 1] = code_pair4_int<1>(w[j], hi);
+        out[4 * j + 2] = code_pair4_int<2>(w[j], hi);
+        out[4 * j + 3] = code_pair4_int<3>(w[j], hi);
+    }
+}
+
 // Widen NCODES codes (stored from bit 0 of w) into NCODES/2 fp16 pairs in
-// pair order: exact integers for 2, 3, 5, 6 and 8 bits, 64 + code for 4 bits.
+// pair order: exact integers for 2, 3, 5, 6 and 8 bits, q * 2^-20 for 4 bits.
 template <int BITS, int NCODES, int NW>
 __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&out)[NCODES / 2])
 {
@@ -190,34 +227,19 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[NW], half2_t (&
 // ---------------------------------------------------------------------------
 // bf16 widening (activations, scales and biases in bf16).
 //
-// A bf16 number has 7 fraction bits. 4-bit codes use the exponent trick of
-// the fp16 route with the code in fraction bits 3..6 under 2^4, so a half
-// becomes 16 + code exactly; pairs are again codes (k, k + 4) of a word (four
-// shifts and four v_and_or_b32 per word) and the epilogue folds the 16 into
-// the bias. Other widths do not fit a 7-bit fraction with a usable pairing
-// (8-bit codes not at all): each code is extracted, converted to fp32 and two
-// codes are packed to bf16 with round-to-nearest, exact because every code is
-// an integer below 2^8. Those pairs hold consecutive codes (2i, 2i + 1).
+// A bf16 number has 7 fraction bits and no exponent trick leaves a code
+// without an offset except a subnormal, whose products with bf16 activations
+// would fall among the fp32 subnormals. Codes are therefore converted
+// exactly: each code becomes an fp32 integer and two of them are packed to
+// bf16 with round-to-nearest (exact, every code is an integer below 2^8).
+// For 4-bit codes the nibbles are first split into the bytes of two words
+// (codes 0, 2, 4, 6 and 1, 3, 5, 7), so that every code converts with one
+// v_cvt_f32_ubyte; other widths extract each code with a bit-field read.
+// Pairs hold consecutive codes (2i, 2i + 1) and the activations keep their
+// natural order.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-template <int P>
-__device__ __forceinline__ bf16x2_t code_pair4_bf16(uint32_t word)
-{
-    constexpr uint32_t mask = 0x00780078u;   // fraction bits 3..6 of each half
-    constexpr uint32_t magic = 0x41804180u;  // 2^4 in each half
-    uint32_t v;
-    if constexpr (P == 0)
-        v = word << 3;
-    else if constexpr (P == 1)
-        v = word >> 1;
-    else if constexpr (P == 2)
-        v = word >> 5;
-    else
-        v = word >> 9;
-    return __builtin_bit_cast(bf16x2_t, and_or(v, mask, magic));
-}
 
 // Code k of a run of codes stored from bit 0 of w.
 template <int BITS, int K, int NW>
@@ -227,24 +249,36 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW])
     return stream_window<K * BITS>(w) & ((1u << BITS) - 1u);
 }
 
-template <int BITS>
-struct CodeOffsetBf16 {
-    static constexpr float value = BITS == 4 ? 16.0f : 0.0f;
-};
+// Pair P (codes 2P, 2P + 1) of the 8 codes of a 4-bit word, from the word's
+// even nibbles (lo = w & 0x0F0F0F0F) and odd nibbles (hi = (w >> 4) & ...).
+template <int P>
+__device__ __forceinline__ bf16x2_t code_pair4_bf16(uint32_t lo, uint32_t hi)
+{
+    const float a = (float)((lo >> (8 * P)) & 0xffu);
+    const float b = (float)((hi >> (8 * P)) & 0xffu);
+    return bf16x2_t{(__bf16)a, (__bf16)b};
+}
 
 template <int BITS, int NW, int... Ps>
 __device__ __forceinline__ void unpack_pairs_bf16_impl(const uint32_t (&w)[NW], bf16x2_t *out,
                                                        std::integer_sequence<int, Ps...>)
 {
-    if constexpr (BITS == 4)
-        ((out[Ps] = code_pair4_bf16<Ps % 4>(w[Ps / 4])), ...);
-    else
+    if constexpr (BITS == 4) {
+        uint32_t lo[NW], hi[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            lo[j] = w[j] & 0x0F0F0F0Fu;
+            hi[j] = (w[j] >> 4) & 0x0F0F0F0Fu;
+        }
+        ((out[Ps] = code_pair4_bf16<Ps % 4>(lo[Ps / 4], hi[Ps / 4])), ...);
+    } else {
         ((out[Ps] = bf16x2_t{(__bf16)(float)code_at<BITS, 2 * Ps>(w),
                              (__bf16)(float)code_at<BITS, 2 * Ps + 1>(w)}), ...);
+    }
 }
 
-// Widen NCODES codes into NCODES/2 bf16 pairs: 16 + code in pair order for
-// 4 bits, exact codes in natural order otherwise.
+// Widen NCODES codes into NCODES/2 bf16 pairs of exact integers in natural
+// order.
 template <int BITS, int NCODES, int NW>
 __device__ __forceinline__ void unpack_pairs_bf16(const uint32_t (&w)[NW], bf16x2_t (&out)[NCODES / 2])
 {
@@ -253,14 +287,11 @@ __device__ __forceinline__ void unpack_pairs_bf16(const uint32_t (&w)[NW], bf16x
 }
 
 // The 8 activations of a unit (bf16 bit patterns) in the order of
-// unpack_pairs_bf16: pair order for 4-bit codes, natural otherwise.
+// unpack_pairs_bf16: natural order.
 template <int BITS>
 __device__ __forceinline__ half8_t to_pair_order_bf16(half8_t v)
 {
-    if constexpr (BITS == 4)
-        return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
-    else
-        return v;
+    return v;
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h16)
@@ -318,6 +349,21 @@ template <typename T>
 __device__ __forceinline__ void pin_register(T &v)
 {
     asm volatile("" : "+v"(v));
+}
+
+// Lanes of one wave that hand data to each other through LDS (one lane
+// writes, other lanes of the same wave read, or a region is rewritten after
+// other lanes read it) need no workgroup barrier: a wave's LDS instructions
+// execute in program order. What they need is that the compiler keeps that
+// order: in the per-thread memory model those accesses look unrelated
+// (other lanes' addresses, and different types for the same bytes), so it
+// could otherwise move them past each other. The wavefront-scope fences and
+// the wave barrier pin every LDS access on its side; they emit no wait.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // base + a 32-bit byte offset: with a wave-uniform base this maps onto the

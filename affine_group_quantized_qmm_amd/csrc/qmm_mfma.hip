@@ -303,13 +303,15 @@ void mfma_kernel(const ProductArgs a)
                         P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, P, 0, 0, 0);
                     }
                 }
+                // the widened codes carry 1 / CodeScale (4-bit fp16 codes are
+                // subnormals q * 2^-20); the scale takes it back
                 float s, b;
                 if constexpr (BF16) {
                     s = bf16_bits_to_float(sb[t] & 0xffffu);
-                    b = bf16_bits_to_float(sb[t] >> 16) - CodeOffsetBf16<BITS>::value * s;
+                    b = bf16_bits_to_float(sb[t] >> 16);
                 } else {
-                    s = half_bits_to_float((uint16_t)(sb[t] & 0xffffu));
-                    b = half_bits_to_float((uint16_t)(sb[t] >> 16)) - CodeOffset<BITS>::value * s;
+                    s = half_bits_to_float((uint16_t)(sb[t] & 0xffffu)) * CodeScale<BITS>::value;
+                    b = half_bits_to_float((uint16_t)(sb[t] >> 16));
                 }
 #pragma unroll
                 for (int r = 0; r < RLIVE; ++r)

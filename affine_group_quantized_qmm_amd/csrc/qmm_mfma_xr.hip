@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
 {
     static_assert(!(TILED && BF16), "the tiled layout is fp16 only");
     using Geo = XrGeo<BITS, G, XC>;
+    // factor between the accumulated sums and y (see CodeScale)
+    constexpr float kOutScale = BF16 ? 1.0f : CodeScale<BITS>::value;
     constexpr int CB = tiled_chunk_bytes<BITS, G>();       // tiled: bytes per lane chunk
     constexpr int NIT = (Geo::XG * CB + 15) / 16;          // tiled: 16-byte code loads per lane per tile
     constexpr int T = Geo::T, CH = Geo::CH, GB = Geo::GB, XG = Geo::XG, NI = Geo::NI;
@@ -333,6 +335,7 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 }
             xsl[(g * 4 + c) * 16 + i] = ps;
         }
+        wave_lds_sync();  // the quarters written by the other lane blocks are read below
 #pragma unroll
         for (int u = 0; u < Geo::XQ; ++u) {
             const int g = 4 * u + c;
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
             }
             xsa[u] = v;
         }
+        wave_lds_sync();  // the scratch is rewritten below (zeroed words, staged tiles)
         // scale/bias words of groups past the part stay zero: those groups
         // (computed in whole quads) contribute nothing
         if constexpr (!TILED)
@@ -359,7 +363,9 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     auto process = [&](Stage &sk, int tile) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!TILED) {
+            wave_lds_sync();  // the previous tile's reads of the region are done
             stage_to_lds(sk);
+            wave_lds_sync();  // other lanes read the staged rows below
             // the stage's registers are free again: start the loads NST tiles ahead
             issue(sk, tile + NST);
         }
@@ -434,14 +440,14 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     sbo = sbrow[4 * u + c];
                     sbq = *reinterpret_cast<const u32x4 *>(sbrow + 4 * u);
                 }
-                float so, bo;
-                if constexpr (BF16) {
-                    so = bf16_bits_to_float(sbo & 0xffffu);
-                    bo = bf16_bits_to_float(sbo >> 16) - CodeOffsetBf16<BITS>::value * so;
-                } else {
-                    so = half_bits_to_float((uint16_t)(sbo & 0xffffu));
-                    bo = half_bits_to_float((uint16_t)(sbo >> 16)) - CodeOffset<BITS>::value * so;
-                }
+                // acc carries the factor 1 / kOutScale of the widened codes
+                // (4-bit fp16 codes are subnormals q * 2^-20), so the bias
+                // enters scaled by it (exact: a power of two)
+                float bo;
+                if constexpr (BF16)
+                    bo = bf16_bits_to_float(sbo >> 16);
+                else
+                    bo = half_bits_to_float((uint16_t)(sbo >> 16)) * CodeScale<BITS>::inverse;
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsa[u], bo, acc, 0, 0, 0);
                 // scale term: acc += s[n][g] * P_g
 #pragma unroll
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                         v += red_at(buf, sl, p, r);
                     const int m = 4 * c + r;
                     if (col < N && m < M)
-                        yout[(size_t)m * N + col] = v;
+                        yout[(size_t)m * N + col] = v * kOutScale;
                 }
             }
         }

@@ -231,23 +231,30 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                 const int gl = lam + sl * LPR;
                 const int glc = min(gl, ng - 1);
                 const uint32_t sb = sbl[wave * RPW + r * RPI + rho][glc];
+                // codes are widened to exact fp16 (or bf16) integers: v_dot2
+                // loses precision on subnormal operands (see code_pair4_int)
                 float sc, bias;
                 if constexpr (BF16) {
                     sc = bf16_bits_to_float(sb & 0xffffu);
-                    bias = bf16_bits_to_float(sb >> 16) - CodeOffsetBf16<BITS>::value * sc;
+                    bias = bf16_bits_to_float(sb >> 16);
                 } else {
                     sc = half_bits_to_float((uint16_t)(sb & 0xffffu));
-                    bias = half_bits_to_float((uint16_t)(sb >> 16)) - CodeOffset<BITS>::value * sc;
+                    bias = half_bits_to_float((uint16_t)(sb >> 16));
                 }
+                constexpr bool kTwoChains = !BF16 && BITS == 4;
                 half2_t q[NPAIR];
                 bf16x2_t qb[NPAIR];
                 if constexpr (BF16)
                     unpack_pairs_bf16<BITS, G>(st.w, qb);
+                else if constexpr (BITS == 4)
+                    unpack_pairs4_int<G>(st.w, q);
                 else
                     unpack_pairs<BITS, G>(st.w, q);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                    float P = 0.f;
+                    // two accumulators for 4-bit codes (even and odd pairs, two
+                    // independent v_dot2 chains), added below
+                    float Pa = 0.f, Pb = 0.f;
 #pragma unroll
                     for (int u = 0; u < UPG; ++u) {
                         const half8_t xv = xp[m][u][glc];
@@ -255,12 +262,15 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                         for (int e = 0; e < 4; ++e) {
                             const half2_t xe = {xv[2 * e], xv[2 * e + 1]};
                             if constexpr (BF16)
-                                P = __builtin_amdgcn_fdot2_f32_bf16(qb[4 * u + e], __builtin_bit_cast(bf16x2_t, xe), P,
-                                                                    false);
+                                Pa = __builtin_amdgcn_fdot2_f32_bf16(qb[4 * u + e], __builtin_bit_cast(bf16x2_t, xe),
+                                                                     Pa, false);
+                            else if (kTwoChains && e % 2 == 1)
+                                Pb = __builtin_amdgcn_fdot2(q[4 * u + e], xe, Pb, false);
                             else
-                                P = __builtin_amdgcn_fdot2(q[4 * u + e], xe, P, false);
+                                Pa = __builtin_amdgcn_fdot2(q[4 * u + e], xe, Pa, false);
                         }
                     }
+                    const float P = kTwoChains ? Pa + Pb : Pa;
                     // explicit fma: the same rounding in every instantiation
                     const float contrib = __builtin_fmaf(sc, P, bias * xsum[m][glc]);
                     acc[m][r] += gl < ng ? contrib : 0.f;
