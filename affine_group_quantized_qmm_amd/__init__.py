@@ -35,6 +35,7 @@ _lib.qmm_forward.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_rowexact.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_bf16.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_splitk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]
+_lib.qmm_forward_splitk_noalloc.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_kernel.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_forward_fused.argtypes = [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
 _lib.qmm_tiled_bytes.argtypes = [_i, _i, _i, _i, ctypes.POINTER(_sz)]
@@ -49,12 +50,13 @@ _lib.qmm_strerror.restype = ctypes.c_char_p
 _lib.qmm_kernel_name.argtypes = [_i, _i, _i, _i, _i]
 _lib.qmm_kernel_name.restype = ctypes.c_char_p
 for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_bf16,
-           _lib.qmm_forward_splitk,
+           _lib.qmm_forward_splitk, _lib.qmm_forward_splitk_noalloc,
            _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_repack_tiled,
            _lib.qmm_forward_tiled, _lib.qmm_validate):
     _f.restype = _i
 
 EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_bf16", "qmm_forward_splitk",
+            "qmm_forward_splitk_noalloc",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
             "qmm_forward_kernel", "qmm_forward_fused", "qmm_tiled_bytes", "qmm_repack_tiled",
             "qmm_forward_tiled")
@@ -63,6 +65,8 @@ QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 
 
 QMM_ERR_UNSUPPORTED = -9  # qmm_forward_kernel: the named kernel cannot run this shape
+QMM_ERR_SCRATCH = -10     # qmm_forward_splitk_noalloc: partials exceed the static scratch
+QMM_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class QmmError(RuntimeError):
@@ -294,4 +298,20 @@ def qmm_forward_splitk(x, wq, scales, biases, bits: int, G: int, split_k: int,
                                  ws_ptr, ws_bytes, _stream(x))
     if rc:
         raise QmmError(rc, "qmm_forward_splitk")
+    return out
+
+
+def qmm_forward_splitk_noalloc(x, wq, scales, biases, bits: int, G: int, split_k: int,
+                               out=None) -> torch.Tensor:
+    """qmm_forward_splitk with its partials in the library's static scratch
+    (the library allocates nothing; `out` may be preallocated by the caller)."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (M, N), dev)
+    rc = _lib.qmm_forward_splitk_noalloc(x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+                                         biases.data_ptr(), out.data_ptr(), M, K, N, bits, G,
+                                         split_k, _stream(x))
+    if rc:
+        raise QmmError(rc, "qmm_forward_splitk_noalloc")
     return out

@@ -112,6 +112,54 @@ int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uin
     return launch_args(kind, product_args(x, wq, scales, biases, y, M, K, N, split), bits, G, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of qmm_forward_splitk_noalloc: the fp32 split-K partials of
+// callers that cannot allocate device memory. Every device that loads the
+// library holds its own copy until the process ends. In host code the
+// array's name is only a host-side stand-in, never a device address: the
+// device address is looked up once per device with hipGetSymbolAddress
+// (scratch_on_device) and only that address reaches the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[QMM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+std::atomic<float *> scratch_address[64];  // per device ordinal; null until looked up
+
+// Device address of `scratch` on the current device. Racing first calls
+// look it up twice and store the same value.
+int scratch_on_device(float **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return QMM_ERR_LAUNCH;
+    float *p = scratch_address[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr)
+            return QMM_ERR_LAUNCH;
+        p = static_cast<float *>(addr);
+        scratch_address[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return QMM_OK;
+}
+
+// The split-K product with `workspace` (at least split_k*M*N floats) holding
+// the partials: one slice launch and the in-order reduction.
+int splitk_into(const uint16_t *x, const uint32_t *wq, const uint16_t *scales, const uint16_t *biases,
+                float *y, int M, int K, int N, int bits, int G, int split_k, float *workspace,
+                hipStream_t stream)
+{
+    const Kernel kind = choose_kernel(M, K, N, bits, G, split_k);
+    if (split_k == 1)
+        return launch_product(kind, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
+    const int rc = launch_product(kind, x, wq, scales, biases, workspace, M, K, N, bits, G, split_k, stream);
+    if (rc != QMM_OK)
+        return rc;
+    return qmm::launch_splitk_reduce(workspace, y, split_k, (size_t)M * N, stream) == hipSuccess
+               ? QMM_OK
+               : QMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 namespace qmm {
@@ -148,6 +196,7 @@ const char *qmm_strerror(int code)
     case QMM_ERR_ALIGN: return "x, wq, scales, biases, y and workspace must be 16-byte aligned";
     case QMM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case QMM_ERR_UNSUPPORTED: return "the requested kernel cannot run this shape";
+    case QMM_ERR_SCRATCH: return "split_k * M * N * 4 bytes exceed the static scratch (QMM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
     }
 }
@@ -221,16 +270,27 @@ int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *sc
                                 split_k < 1 ? -1 : split_k, workspace, workspace_bytes);
     if (rc != QMM_OK)
         return rc;
-    const Kernel kind = choose_kernel(M, K, N, bits, G, split_k);
-    if (split_k == 1)
-        return launch_product(kind, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
-    const int rc1 = launch_product(kind, x, wq, scales, biases, workspace, M, K, N, bits, G,
-                                   split_k, stream);
-    if (rc1 != QMM_OK)
-        return rc1;
-    return qmm::launch_splitk_reduce(workspace, y, split_k, (size_t)M * N, stream) == hipSuccess
-               ? QMM_OK
-               : QMM_ERR_LAUNCH;
+    return splitk_into(x, wq, scales, biases, y, M, K, N, bits, G, split_k, workspace, stream);
+}
+
+int qmm_forward_splitk_noalloc(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                               const uint16_t *biases, float *y, int M, int K, int N, int bits,
+                               int G, int split_k, hipStream_t stream)
+{
+    int rc = qmm_validate(x, wq, scales, biases, y, M, K, N, bits, G, 0, nullptr, 0);
+    if (rc != QMM_OK)
+        return rc;
+    if (split_k < 1 || split_k > K / G)
+        return QMM_ERR_SPLIT;
+    if (qmm_splitk_workspace_bytes(M, N, split_k) > (size_t)QMM_NOALLOC_SCRATCH_BYTES)
+        return QMM_ERR_SCRATCH;
+    float *ws = nullptr;
+    if (split_k > 1) {
+        rc = scratch_on_device(&ws);
+        if (rc != QMM_OK)
+            return rc;
+    }
+    return splitk_into(x, wq, scales, biases, y, M, K, N, bits, G, split_k, ws, stream);
 }
 
 int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,

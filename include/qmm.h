@@ -37,17 +37,21 @@
  * M = 1..16 verify rows; larger M is processed 16 rows at a time).
  *
  * Ownership: the caller owns every buffer. Functions without a workspace
- * argument need no scratch memory; no entry point allocates device memory.
- * Work is enqueued on the caller's stream and the call returns without
- * waiting; results are visible after the stream is synchronized.
+ * argument need no scratch memory, except qmm_forward_splitk_noalloc, which
+ * uses a static array of the library (QMM_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from module load to process end); no entry point allocates device
+ * memory. Work is enqueued on the caller's stream and the call returns
+ * without waiting; results are visible after the stream is synchronized.
  *
  * Errors: every entry point validates its arguments on the host before any
  * GPU work and returns 0 on success or one of the negative codes below.
  * Argument errors launch nothing. A launch failure reported by the HIP
  * runtime returns QMM_ERR_LAUNCH; execution faults surface at stream
  * synchronization as with any HIP kernel. No exception or abort crosses
- * this interface. The library is stateless and may be called from several
- * host threads at once.
+ * this interface. The library keeps no state between calls other than
+ * cached device properties and the per-GPU address of that static array; it
+ * may be called from several host threads at once (with the caveat on
+ * qmm_forward_splitk_noalloc's shared scratch).
  */
 #ifndef QMM_H
 #define QMM_H
@@ -70,6 +74,7 @@ extern "C" {
 #define QMM_ERR_ALIGN (-7)         /* x, wq, scales, biases, y or workspace not 16-byte aligned */
 #define QMM_ERR_LAUNCH (-8)        /* the HIP runtime rejected a kernel launch */
 #define QMM_ERR_UNSUPPORTED (-9)   /* qmm_forward_kernel: that kernel cannot run this shape */
+#define QMM_ERR_SCRATCH (-10)      /* qmm_forward_splitk_noalloc: partials exceed the static scratch */
 
 /*
  * qmm_pack - pack unpacked codes into the bitstream layout above.
@@ -124,6 +129,32 @@ int qmm_forward_splitk(const uint16_t *x, const uint32_t *wq, const uint16_t *sc
                        const uint16_t *biases, float *y, int M, int K, int N, int bits,
                        int G, int split_k, float *workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/*
+ * qmm_forward_splitk_noalloc - qmm_forward_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the fp32 partials go to a static scratch
+ * array inside the library instead of a caller workspace.
+ *
+ * Arguments, layout, slices, kernels and results are those of
+ * qmm_forward_splitk (bitwise equal to it for the same arguments), without
+ * the workspace arguments. The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine. Requires
+ * split_k * M * N * 4 <= QMM_NOALLOC_SCRATCH_BYTES, else QMM_ERR_SCRATCH
+ * (checked on the host, nothing is launched); split_k == 1 uses no scratch.
+ *
+ * The scratch is one array per GPU, kept until the process ends; its device
+ * address is looked up on the first call on each device. Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (several streams or
+ * host threads without ordering between them) race on it and must be
+ * serialized by the caller. Each call overwrites every partial it reads, so
+ * nothing needs clearing between calls. Errors as qmm_forward_splitk, plus
+ * QMM_ERR_SCRATCH; QMM_ERR_LAUNCH if the scratch address cannot be found.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES (16u << 20)  /* 16 MiB per GPU */
+int qmm_forward_splitk_noalloc(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                               const uint16_t *biases, float *y, int M, int K, int N, int bits,
+                               int G, int split_k, hipStream_t stream);
 
 /* Row-exact product (vmlx-swift pull request #565 page, commit introducing
  * qwen_qmv_rows_full: every verify row keeps the one-row kernel's statement

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_error_codes_and_messages():
-    for code in range(0, -9, -1):
+    for code in range(0, -11, -1):
         assert qmm.qmm_strerror(code) and "unknown" not in qmm.qmm_strerror(code)
     assert "unknown" in qmm.qmm_strerror(-99)
 
