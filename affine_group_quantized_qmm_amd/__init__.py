@@ -42,6 +42,9 @@ _lib.qmm_tiled_bytes.argtypes = [_i, _i, _i, _i, ctypes.POINTER(_sz)]
 _lib.qmm_tiled_bytes.restype = _sz
 _lib.qmm_repack_tiled.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
 _lib.qmm_forward_tiled.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.qmm_stream_read.argtypes = [_p, _sz, _p, _p]
+_lib.qmm_stream_read_sink_words.argtypes = [_sz]
+_lib.qmm_stream_read_sink_words.restype = _sz
 _lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.qmm_splitk_workspace_bytes.restype = _sz
 _lib.qmm_validate.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz]
@@ -52,14 +55,14 @@ _lib.qmm_kernel_name.restype = ctypes.c_char_p
 for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_bf16,
            _lib.qmm_forward_splitk, _lib.qmm_forward_splitk_noalloc,
            _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_repack_tiled,
-           _lib.qmm_forward_tiled, _lib.qmm_validate):
+           _lib.qmm_forward_tiled, _lib.qmm_validate, _lib.qmm_stream_read):
     _f.restype = _i
 
 EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_bf16", "qmm_forward_splitk",
             "qmm_forward_splitk_noalloc",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
             "qmm_forward_kernel", "qmm_forward_fused", "qmm_tiled_bytes", "qmm_repack_tiled",
-            "qmm_forward_tiled")
+            "qmm_forward_tiled", "qmm_stream_read", "qmm_stream_read_sink_words")
 
 QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 
@@ -279,6 +282,26 @@ def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,
     if rc:
         raise QmmError(rc, "qmm_forward_kernel")
     return out
+
+
+def qmm_stream_read_sink_words(nbytes: int) -> int:
+    return int(_lib.qmm_stream_read_sink_words(nbytes))
+
+
+def qmm_stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Streaming-read ceiling: reads every byte of the contiguous GPU tensor
+    `src` once; returns the int32 sink (one XOR word per 64 KiB span)."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    words = qmm_stream_read_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _check(sink, "sink", _WORD_DTYPES, (max(words, 1),), src.device)
+    rc = _lib.qmm_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src))
+    if rc:
+        raise QmmError(rc, "qmm_stream_read")
+    return sink
 
 
 def qmm_forward_splitk(x, wq, scales, biases, bits: int, G: int, split_k: int,

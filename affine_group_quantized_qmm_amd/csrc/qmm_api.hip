@@ -419,6 +419,22 @@ int qmm_forward_tiled(const uint16_t *x, const uint8_t *tiled_w, const uint32_t 
     return QMM_OK;
 }
 
+size_t qmm_stream_read_sink_words(size_t bytes)
+{
+    return bytes == 0 || bytes % 16 != 0 ? 0 : qmm::stream_read_sink_words(bytes);
+}
+
+int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (!src || !sink)
+        return QMM_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || qmm::stream_read_sink_words(bytes) > 0x7FFFFFFFu)
+        return QMM_ERR_SHAPE;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return QMM_ERR_ALIGN;
+    return qmm::launch_stream_read(src, bytes, sink, stream) == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq,
                        const uint16_t *scales, const uint16_t *biases, float *y, int M, int K,
                        int N, int bits, int G, hipStream_t stream)

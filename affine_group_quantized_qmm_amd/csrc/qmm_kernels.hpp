@@ -100,6 +100,10 @@ bool tiled_supported(const ProductArgs &a, int bits, int G);
 hipError_t launch_repack_tiled(const uint32_t *wq, const uint16_t *scales, const uint16_t *biases, uint8_t *tw,
                                uint32_t *tsb, int N, int K, int bits, int G, hipStream_t stream);
 hipError_t launch_mfma_tiled(const ProductArgs &a, int bits, int G, hipStream_t stream);
+// Streaming read of `bytes` (a multiple of 16) at `src` (16-byte aligned):
+// one sink word per workgroup, stream_read_sink_words(bytes) in all.
+size_t stream_read_sink_words(size_t bytes);
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size_t count,
                                 hipStream_t stream);
 

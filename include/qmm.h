@@ -281,6 +281,25 @@ int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq
                        const uint16_t *scales, const uint16_t *biases, float *y, int M,
                        int K, int N, int bits, int G, hipStream_t stream);
 
+/* Streaming-read ceiling (a measurement aid, not part of the product): reads
+ * the `bytes` bytes at `src` once, with the 16-byte non-temporal loads the
+ * product kernels use for packed codes, every load of a thread issued before
+ * any is used, and writes one word per workgroup to `sink`: the XOR of the
+ * 32-bit words that workgroup read (workgroup w reads the 64 KiB span
+ * starting at byte w * 65536; the last span may be short). Its time bounds
+ * what any kernel that must read those bytes can reach on this GPU, which is
+ * how the one-row product's weight stream is judged (it reads each weight
+ * byte once and writes almost nothing).
+ *   src   device memory, 16-byte aligned; bytes a positive multiple of 16;
+ *   sink  device memory of qmm_stream_read_sink_words(bytes) uint32 words,
+ *         4-byte aligned, overwritten.
+ * Errors: QMM_ERR_NULL, QMM_ERR_SHAPE (bytes 0 or not a multiple of 16),
+ * QMM_ERR_ALIGN, QMM_ERR_LAUNCH. Async on `stream`.
+ * qmm_stream_read_sink_words: the sink's length in words; 0 for an invalid
+ * byte count. Host-only. */
+size_t qmm_stream_read_sink_words(size_t bytes);
+int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

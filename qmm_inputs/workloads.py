@@ -70,5 +70,11 @@ def sweep_shapes(layers: int = SWEEP_LAYERS):
             yield layer, j, Shape(f"L{layer}.{pname}", K=K, N=N, bits=4, G=32), 1000 * layer + j
 
 
+def sweep_x_seed(layer: int, key: int, M: int) -> int:
+    """Seed of the M-row input `key` of a sweep layer (0: q/k/v, 1: o,
+    2: gate/up, 3: down; q/k/v and gate/up share their input)."""
+    return 500_000 + 100 * layer + 10 * key + M
+
+
 def sweep_weight_bytes(layers: int = SWEEP_LAYERS) -> int:
     return sum(s.weight_bytes for _, _, s, _ in sweep_shapes(layers))

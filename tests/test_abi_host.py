@@ -7,11 +7,12 @@ from pathlib import Path
 
 import pytest
 
+# A missing libqmm.so is a failure here (ImportError at collection), not a skip:
+# these checks are what shows that the boundary exists at all.
+import affine_group_quantized_qmm_amd as qmm
+
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "qmm.h"
-
-qmm = pytest.importorskip("affine_group_quantized_qmm_amd",
-                          reason="libqmm.so not built (run __graft_entry__.build())")
 
 
 def declared_functions():
@@ -137,3 +138,18 @@ def test_tiled_sizes_and_rejections():
     assert lib.qmm_forward_tiled(16, 16, 16, 16, 1, 512, 16, 3, 32, None) == -9
     assert lib.qmm_forward_tiled(16, 16, 16, 16, 1, 416, 16, 4, 32, None) == -9
     assert lib.qmm_forward_tiled(16, 16, None, 16, 1, 512, 16, 4, 32, None) == -1
+
+
+def test_stream_read_rejects_before_launch():
+    lib = qmm._lib
+    assert qmm.qmm_stream_read_sink_words(0) == 0
+    assert qmm.qmm_stream_read_sink_words(40) == 0
+    assert qmm.qmm_stream_read_sink_words(16) == 1
+    assert qmm.qmm_stream_read_sink_words(65536) == 1
+    assert qmm.qmm_stream_read_sink_words(65536 + 16) == 2
+    assert lib.qmm_stream_read(None, 64, A, None) == -1
+    assert lib.qmm_stream_read(A, 64, None, None) == -1
+    assert lib.qmm_stream_read(A, 0, A, None) == -2
+    assert lib.qmm_stream_read(A, 40, A, None) == -2
+    assert lib.qmm_stream_read(A + 4, 64, A, None) == -7
+    assert lib.qmm_stream_read(A, 64, A + 2, None) == -7
