@@ -79,12 +79,22 @@ extern "C" {
 /*
  * qmm_pack - pack unpacked codes into the bitstream layout above.
  *
+ * The pages' quantized tensors are packed once and then consumed in their
+ * stored form by every product ("Qwen3.8 Flash Next performance and parity
+ * receipt" page, section "MTPLX logic review": its 4-bit group-32 and
+ * group-64, 8-bit and 2-bit tensors are used in their stored form, neither
+ * up-converted nor re-quantized). This is that one-time packing step, into
+ * the layout defined at the top of this header, which every entry point then
+ * reads as is.
+ *
  * codes  [N, K] uint8, device memory; only the low `bits` bits of each byte
  *        are stored (higher bits are ignored).
- * packed [N, K*bits/32] uint32, device memory, written in full.
+ * packed [N, K*bits/32] uint32, device memory, 16-byte aligned, written in
+ *        full. The caller owns both buffers.
  * Requires K*bits to be a multiple of 32 (true whenever 32 divides K).
- * Packing is offline work (weights are packed once and then consumed as
- * stored); it is bit-exact with respect to the layout definition.
+ * Bit-exact with respect to the layout definition. Errors: QMM_ERR_NULL,
+ * QMM_ERR_BITS, QMM_ERR_SHAPE (N < 1, K < 1, K*bits not a multiple of 32),
+ * QMM_ERR_ALIGN, QMM_ERR_LAUNCH. Async on `stream`.
  */
 int qmm_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,
              hipStream_t stream);
