@@ -43,6 +43,13 @@ _lib.qmm_tiled_bytes.restype = _sz
 _lib.qmm_repack_tiled.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
 _lib.qmm_forward_tiled.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.qmm_stream_read.argtypes = [_p, _sz, _p, _p]
+_lib.qmm_admit_workspace_bytes.argtypes = [_i, _i]
+_lib.qmm_admit_workspace_bytes.restype = _sz
+_lib.qmm_admit.argtypes = [ctypes.c_char_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p,
+                           ctypes.POINTER(_i)]
+_lib.qmm_admission.argtypes = [ctypes.c_char_p, _i, _i, _i, _i, _i]
+_lib.qmm_admission_clear.argtypes = []
+_lib.qmm_admission_clear.restype = None
 _lib.qmm_stream_read_sink_words.argtypes = [_sz]
 _lib.qmm_stream_read_sink_words.restype = _sz
 _lib.qmm_splitk_workspace_bytes.argtypes = [_i, _i, _i]
@@ -55,14 +62,16 @@ _lib.qmm_kernel_name.restype = ctypes.c_char_p
 for _f in (_lib.qmm_pack, _lib.qmm_forward, _lib.qmm_forward_rowexact, _lib.qmm_forward_bf16,
            _lib.qmm_forward_splitk, _lib.qmm_forward_splitk_noalloc,
            _lib.qmm_forward_kernel, _lib.qmm_forward_fused, _lib.qmm_repack_tiled,
-           _lib.qmm_forward_tiled, _lib.qmm_validate, _lib.qmm_stream_read):
+           _lib.qmm_forward_tiled, _lib.qmm_validate, _lib.qmm_stream_read, _lib.qmm_admit,
+           _lib.qmm_admission):
     _f.restype = _i
 
 EXPORTED = ("qmm_pack", "qmm_forward", "qmm_forward_rowexact", "qmm_forward_bf16", "qmm_forward_splitk",
             "qmm_forward_splitk_noalloc",
             "qmm_splitk_workspace_bytes", "qmm_validate", "qmm_strerror", "qmm_kernel_name",
             "qmm_forward_kernel", "qmm_forward_fused", "qmm_tiled_bytes", "qmm_repack_tiled",
-            "qmm_forward_tiled", "qmm_stream_read", "qmm_stream_read_sink_words")
+            "qmm_forward_tiled", "qmm_stream_read", "qmm_stream_read_sink_words",
+            "qmm_admit_workspace_bytes", "qmm_admit", "qmm_admission", "qmm_admission_clear")
 
 QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 
@@ -70,6 +79,7 @@ QMM_MAX_FUSED = 4  # projections per qmm_forward_fused call
 QMM_ERR_UNSUPPORTED = -9  # qmm_forward_kernel: the named kernel cannot run this shape
 QMM_ERR_SCRATCH = -10     # qmm_forward_splitk_noalloc: partials exceed the static scratch
 QMM_NOALLOC_SCRATCH_BYTES = 16 << 20
+QMM_ADMISSION_UNKNOWN = 2  # qmm_admission: the shape was never examined
 
 
 class QmmError(RuntimeError):
@@ -282,6 +292,39 @@ def qmm_forward_kernel(kernel: str, x, wq, scales, biases, bits: int, G: int,
     if rc:
         raise QmmError(rc, "qmm_forward_kernel")
     return out
+
+
+def qmm_admit_workspace_bytes(M: int, N: int) -> int:
+    return int(_lib.qmm_admit_workspace_bytes(M, N))
+
+
+def qmm_admit(kind: str, x, wq, scales, biases, bits: int, G: int, workspace=None) -> bool:
+    """Bitwise admission of `kind` ("rowexact" or "forward") against one-row
+    launches on these inputs; records and returns the verdict (waits for the
+    current stream)."""
+    M, K, N, dev = _operands(x, wq, scales, biases, bits, G)
+    need = qmm_admit_workspace_bytes(M, N)
+    if workspace is None:
+        workspace = torch.empty(-(-need // 4), dtype=torch.float32, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    out = ctypes.c_int(-1)
+    rc = _lib.qmm_admit(kind.encode(), x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                        M, K, N, bits, G, workspace.data_ptr(), nbytes, _stream(x), ctypes.byref(out))
+    if rc:
+        raise QmmError(rc, "qmm_admit")
+    return bool(out.value)
+
+
+def qmm_admission(kind: str, M: int, K: int, N: int, bits: int, G: int) -> int:
+    """1 admitted, 0 rejected, QMM_ADMISSION_UNKNOWN never examined (host-only)."""
+    rc = _lib.qmm_admission(kind.encode(), M, K, N, bits, G)
+    if rc < 0:
+        raise QmmError(rc, "qmm_admission")
+    return rc
+
+
+def qmm_admission_clear() -> None:
+    _lib.qmm_admission_clear()
 
 
 def qmm_stream_read_sink_words(nbytes: int) -> int:

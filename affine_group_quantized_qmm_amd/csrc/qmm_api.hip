@@ -7,6 +7,9 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace {
 
@@ -110,6 +113,47 @@ int launch_product(Kernel kind, const uint16_t *x, const uint32_t *wq, const uin
                    int split, hipStream_t stream)
 {
     return launch_args(kind, product_args(x, wq, scales, biases, y, M, K, N, split), bits, G, stream);
+}
+
+// The original one-row kernel, once per row: the reference a multi-row
+// kernel is admitted against.
+int launch_rows_one_by_one(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                           const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,
+                           hipStream_t stream)
+{
+    const qmm::ProductArgs full = product_args(x, wq, scales, biases, y, M, K, N, 1);
+    for (int m = 0; m < M; ++m)
+        if (qmm::launch_qmv(qmm::rows_of(full, m, 1), bits, G, false, stream) != hipSuccess)
+            return QMM_ERR_LAUNCH;
+    return QMM_OK;
+}
+
+// Admission verdicts per (kind, K, N, M, bits, G): 1 admitted, 0 rejected.
+enum class AdmitKind { rowexact, forward };
+using AdmitKey = std::tuple<int, int, int, int, int, int>;
+std::mutex admit_mutex;
+std::map<AdmitKey, int> &admit_table()
+{
+    static std::map<AdmitKey, int> table;
+    return table;
+}
+
+bool admit_kind(const char *name, AdmitKind &k)
+{
+    if (strcmp(name, "rowexact") == 0)
+        k = AdmitKind::rowexact;
+    else if (strcmp(name, "forward") == 0)
+        k = AdmitKind::forward;
+    else
+        return false;
+    return true;
+}
+
+int admission_of(AdmitKind k, int M, int K, int N, int bits, int G)
+{
+    std::lock_guard<std::mutex> lock(admit_mutex);
+    const auto it = admit_table().find(std::make_tuple((int)k, K, N, M, bits, G));
+    return it == admit_table().end() ? QMM_ADMISSION_UNKNOWN : it->second;
 }
 
 // ---------------------------------------------------------------------------
@@ -300,7 +344,72 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
     const int rc = qmm_validate(x, wq, scales, biases, y, M, K, N, bits, G, 0, nullptr, 0);
     if (rc != QMM_OK)
         return rc;
+    if (M > 1 && admission_of(AdmitKind::rowexact, M, K, N, bits, G) == 0)
+        return launch_rows_one_by_one(x, wq, scales, biases, y, M, K, N, bits, G, stream);
     return launch_product(Kernel::qmv, x, wq, scales, biases, y, M, K, N, bits, G, 1, stream);
+}
+
+size_t qmm_admit_workspace_bytes(int M, int N)
+{
+    if (M < 1 || N < 1 || M >= (1 << 30) || N >= (1 << 30))
+        return 0;
+    return 2 * (size_t)M * N * sizeof(float) + 16;
+}
+
+int qmm_admit(const char *kind, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+              const uint16_t *biases, int M, int K, int N, int bits, int G, void *workspace,
+              size_t workspace_bytes, hipStream_t stream, int *admitted)
+{
+    if (!kind || !admitted || !workspace)
+        return QMM_ERR_NULL;
+    AdmitKind k;
+    if (!admit_kind(kind, k))
+        return QMM_ERR_SHAPE;
+    // y is checked as the workspace (both results live there)
+    const int rc = qmm_validate(x, wq, scales, biases, workspace, M, K, N, bits, G, 0, nullptr, 0);
+    if (rc != QMM_OK)
+        return rc;
+    if (workspace_bytes < qmm_admit_workspace_bytes(M, N))
+        return QMM_ERR_WORKSPACE;
+    float *cand = static_cast<float *>(workspace);
+    float *orig = cand + (size_t)M * N;
+    uint32_t *count = reinterpret_cast<uint32_t *>(orig + (size_t)M * N);
+    int lrc = k == AdmitKind::rowexact
+                  ? launch_product(Kernel::qmv, x, wq, scales, biases, cand, M, K, N, bits, G, 1, stream)
+                  : launch_product(choose_kernel(M, K, N, bits, G, 1), x, wq, scales, biases, cand, M, K, N,
+                                   bits, G, 1, stream);
+    if (lrc != QMM_OK)
+        return lrc;
+    lrc = launch_rows_one_by_one(x, wq, scales, biases, orig, M, K, N, bits, G, stream);
+    if (lrc != QMM_OK)
+        return lrc;
+    if (qmm::launch_compare_words(reinterpret_cast<const uint32_t *>(cand), reinterpret_cast<const uint32_t *>(orig),
+                                  (size_t)M * N, count, stream) != hipSuccess)
+        return QMM_ERR_LAUNCH;
+    uint32_t mismatches = 0;
+    if (hipMemcpyAsync(&mismatches, count, sizeof(mismatches), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return QMM_ERR_LAUNCH;
+    *admitted = mismatches == 0 ? 1 : 0;
+    std::lock_guard<std::mutex> lock(admit_mutex);
+    admit_table()[std::make_tuple((int)k, K, N, M, bits, G)] = *admitted;
+    return QMM_OK;
+}
+
+int qmm_admission(const char *kind, int M, int K, int N, int bits, int G)
+{
+    if (!kind)
+        return QMM_ERR_NULL;
+    AdmitKind k;
+    if (!admit_kind(kind, k))
+        return QMM_ERR_SHAPE;
+    return admission_of(k, M, K, N, bits, G);
+}
+
+void qmm_admission_clear(void)
+{
+    std::lock_guard<std::mutex> lock(admit_mutex);
+    admit_table().clear();
 }
 
 int qmm_forward_bf16(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,

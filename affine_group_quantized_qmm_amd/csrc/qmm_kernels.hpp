@@ -104,6 +104,9 @@ hipError_t launch_mfma_tiled(const ProductArgs &a, int bits, int G, hipStream_t 
 // one sink word per workgroup, stream_read_sink_words(bytes) in all.
 size_t stream_read_sink_words(size_t bytes);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+// *mismatches = number of i < count with a[i] != b[i] (32-bit words).
+hipError_t launch_compare_words(const uint32_t *a, const uint32_t *b, size_t count, uint32_t *mismatches,
+                                hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size_t count,
                                 hipStream_t stream);
 

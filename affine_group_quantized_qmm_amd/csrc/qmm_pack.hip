@@ -46,6 +46,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
+// Number of positions i < count where the 32-bit words a[i] and b[i]
+// differ, written to *mismatches by one workgroup (no atomics, no clearing).
+__global__ __launch_bounds__(256) void compare_words_kernel(const uint32_t *__restrict__ a,
+                                                            const uint32_t *__restrict__ b,
+                                                            size_t count, uint32_t *mismatches)
+{
+    __shared__ uint32_t part[256 / 64];
+    uint32_t n = 0;
+    for (size_t i = threadIdx.x; i < count; i += blockDim.x)
+        n += a[i] != b[i] ? 1u : 0u;
+    for (int d = 32; d >= 1; d /= 2)
+        n += __shfl_xor(n, d);
+    if (threadIdx.x % 64 == 0)
+        part[threadIdx.x / 64] = n;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *mismatches = part[0] + part[1] + part[2] + part[3];
+}
+
 unsigned grid_for(size_t work, unsigned threads)
 {
     const size_t blocks = (work + threads - 1) / threads;
@@ -76,6 +95,13 @@ hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size
 {
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(count, 256)), dim3(256), 0, stream,
                        partials, y, split, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_compare_words(const uint32_t *a, const uint32_t *b, size_t count, uint32_t *mismatches,
+                                hipStream_t stream)
+{
+    hipLaunchKernelGGL(compare_words_kernel, dim3(1), dim3(256), 0, stream, a, b, count, mismatches);
     return hipGetLastError();
 }
 

@@ -177,6 +177,43 @@ int qmm_forward_rowexact(const uint16_t *x, const uint32_t *wq, const uint16_t *
                          const uint16_t *biases, float *y, int M, int K, int N, int bits,
                          int G, hipStream_t stream);
 
+/* Bitwise admission of a multi-row kernel (the same commit of the
+ * vmlx-swift pull request #565 page: a (kind, K, N, rows) is used only after
+ * its output matched the caller's original one-row kernel bit for bit on the
+ * real weights, and a mismatch keeps the original kernel).
+ *
+ * qmm_admit runs the candidate `kind` on x [M,K] and the caller's weights,
+ * runs the original (M launches of the one-row kernel, one row each) on the
+ * same inputs, compares the two fp32 results word for word on the GPU, waits
+ * for the stream and records the verdict for (kind, K, N, M, bits, G) in a
+ * table of the library (per process, shared by every device and thread).
+ * kind: "rowexact" (the multi-row launches of qmm_forward_rowexact) or
+ * "forward" (the kernel qmm_forward chooses for M rows). *admitted receives
+ * 1 (bitwise equal) or 0. workspace: device memory of at least
+ * qmm_admit_workspace_bytes(M, N) bytes, 16-byte aligned, caller-owned, used
+ * for both results and the mismatch count. Other arguments as qmm_forward.
+ * Errors: those of qmm_forward, QMM_ERR_NULL (kind, admitted or workspace
+ * NULL), QMM_ERR_SHAPE (unknown kind), QMM_ERR_WORKSPACE, QMM_ERR_LAUNCH (a
+ * launch, the copy of the count or the wait failed; nothing is recorded).
+ * Synchronous: it returns after `stream` has drained, so it is not for graph
+ * capture; admission is done once per shape, before the serving loop.
+ *
+ * qmm_forward_rowexact keeps its multi-row launches for a (K, N, M, bits, G)
+ * that is admitted or was never examined (the kernel is bitwise by
+ * construction) and falls back to one one-row launch per row when "rowexact"
+ * was rejected for it.
+ *
+ * qmm_admission: the recorded verdict, 1 admitted, 0 rejected, 2 never
+ * examined; QMM_ERR_NULL / QMM_ERR_SHAPE for a NULL or unknown kind.
+ * qmm_admission_clear forgets every verdict. Both are host-only. */
+#define QMM_ADMISSION_UNKNOWN 2
+size_t qmm_admit_workspace_bytes(int M, int N);
+int qmm_admit(const char *kind, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+              const uint16_t *biases, int M, int K, int N, int bits, int G, void *workspace,
+              size_t workspace_bytes, hipStream_t stream, int *admitted);
+int qmm_admission(const char *kind, int M, int K, int N, int bits, int G);
+void qmm_admission_clear(void);
+
 /* bf16 variant (the pages' kernels take bf16 as well as fp16 activations
  * and scales: vmlx-swift pull request #565 page, the split-K verify commit's
  * fp16/bf16 tests and the bf16-activation affine mat-vec of the tiling-policy

@@ -153,3 +153,28 @@ def test_stream_read_rejects_before_launch():
     assert lib.qmm_stream_read(A, 40, A, None) == -2
     assert lib.qmm_stream_read(A + 4, 64, A, None) == -7
     assert lib.qmm_stream_read(A, 64, A + 2, None) == -7
+
+
+def test_admission_table_and_rejections_before_launch():
+    lib = qmm._lib
+    qmm.qmm_admission_clear()
+    assert qmm.qmm_admission("rowexact", 4, 512, 256, 4, 32) == qmm.QMM_ADMISSION_UNKNOWN
+    assert lib.qmm_admission(None, 4, 512, 256, 4, 32) == -1
+    assert lib.qmm_admission(b"nonsense", 4, 512, 256, 4, 32) == -2
+    assert qmm.qmm_admit_workspace_bytes(4, 256) == 2 * 4 * 256 * 4 + 16
+    assert qmm.qmm_admit_workspace_bytes(0, 256) == 0
+    out = ctypes.c_int(-1)
+    need = qmm.qmm_admit_workspace_bytes(4, 256)
+
+    def admit(kind=b"rowexact", ws=A, wsb=need, ptr=ctypes.byref(out), M=4, bits=4):
+        return lib.qmm_admit(kind, A, A, A, A, M, 512, 256, bits, 32, ws, wsb, None, ptr)
+    assert admit(kind=None) == -1
+    assert admit(ptr=None) == -1
+    assert admit(ws=None) == -1
+    assert admit(kind=b"nonsense") == -2
+    assert admit(M=0) == -2
+    assert admit(bits=7) == -3
+    assert admit(wsb=need - 1) == -6
+    assert admit(ws=A + 4) == -7
+    assert out.value == -1  # nothing was recorded or written
+    assert qmm.qmm_admission("rowexact", 4, 512, 256, 4, 32) == qmm.QMM_ADMISSION_UNKNOWN
