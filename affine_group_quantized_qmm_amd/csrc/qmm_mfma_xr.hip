@@ -41,6 +41,11 @@ namespace qmm {
 namespace {
 
 constexpr int kXrMaxParts = 8;    // waves (K parts) per workgroup
+constexpr size_t kXrLdsLimit = 160 * 1024;  // LDS of one CU
+#ifndef XR_MAX_PASSES
+#define XR_MAX_PASSES 8
+#endif
+constexpr int kXrMaxPasses = XR_MAX_PASSES;  // K parts per wave (activations reloaded between them)
 constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after one barrier
 
 // Activations per row held by one wave (XC: 640 or 768, 512 for 8-bit codes,
@@ -89,6 +94,7 @@ struct XrArgs {
     ProductArgs p;
     int gran;    // part boundary granularity in groups
     int ntiles;  // 16-row tiles of N
+    int npass;   // K passes: wave kp owns parts kp, KP + kp, 2 KP + kp, ... of the slice
 };
 
 // Group range [pb, pe) of part kp: the slice [gb, ge) cut into KP parts of
@@ -140,7 +146,10 @@ __host__ __device__ constexpr int tiled_chunk_bytes() { return G * BITS / 32; }
 // the weights goes through LDS.
 // BF16: x, scales and biases hold bf16 bit patterns; codes are widened to
 // bf16 and contracted with v_mfma_f32_16x16x32_bf16.
-template <int BITS, int G, int XC, int SBW, int NST, bool FUSED, bool TILED = false, bool BF16 = false>
+// MP: K passes (xa.npass parts per wave, activations reloaded between them,
+// later passes adding into y); single-pass variants compile the loop away.
+template <int BITS, int G, int XC, int SBW, int NST, bool FUSED, bool TILED = false, bool BF16 = false,
+          bool MP = false>
 __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArgs xa)
 {
     static_assert(!(TILED && BF16), "the tiled layout is fp16 only");
@@ -167,6 +176,9 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     auto red_at = [&](int buf, int slot, int part, int r) -> float & {
         return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
     };
+    // multi-pass: the running sums of the workgroup's tiles between passes,
+    // accl[tile - t0][r][lane], each word read and written by one thread only
+    float *const accl = red + 2 * (size_t)kXrBatch * KP * 4 * kWave;
     const int c = lane / 16, i = lane % 16;
     const int M = a.M, K = a.K, Kg = K / G;
     // projection of a tile; single-projection launches skip the lookup
@@ -181,34 +193,41 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     int gb = 0, ge = Kg;
     if (a.split > 1)
         slice_groups(Kg, a.split, blockIdx.z, gb, ge);
-    int pb, pe;
-    part_range(gb, ge, KP, kp, xa.gran, pb, pe);
-    const int ng = pe - pb;  // >= 1 (the host never makes empty parts)
+    const int npass = (TILED || !MP) ? 1 : xa.npass;
 
     // tiles of this workgroup
     const int t0 = (int)(((long long)blockIdx.x * xa.ntiles) / gridDim.x);
     const int t1 = (int)(((long long)(blockIdx.x + 1) * xa.ntiles) / gridDim.x);
+    const int nbatch = (t1 - t0 + kXrBatch - 1) / kXrBatch;  // barriers per pass
 
-    // Per-lane load geometry, fixed for the launch. Weight unit u (16 bytes)
-    // is row u / U, column u % U of the tile's 16 x (ng*GB) block.
-    const int U = ng * GB / 16;
+    // This wave's K part of the current pass, [pb, pe) (ng >= 1: the host never
+    // makes empty parts), and the per-lane load geometry of that part. Weight
+    // unit u (16 bytes) is row u / U, column u % U of the tile's 16 x (ng*GB)
+    // block.
+    int pb, pe, ng;
     int wr[NI];
     uint32_t wcol[NI], wl[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int u = min(64 * j + lane, 16 * U - 1);
-        wr[j] = u / U;
-        wcol[j] = (uint32_t)pb * GB + (uint32_t)(u % U) * 16;
-        wl[j] = (uint32_t)wr[j] * LSTR + (uint32_t)(u % U) * 16;
-    }
-    const int V = ng / SBE;  // scale/bias units per row (ng is a multiple of SBE)
     int sr[NS], scol[NS];
+    auto set_part = [&](int pass) {
+        part_range(gb, ge, KP * npass, pass * KP + kp, xa.gran, pb, pe);
+        ng = pe - pb;
+        const int U = ng * GB / 16;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        const int e = min(64 * j + lane, 16 * V - 1);
-        sr[j] = e / V;
-        scol[j] = e % V;
-    }
+        for (int j = 0; j < NI; ++j) {
+            const int u = min(64 * j + lane, 16 * U - 1);
+            wr[j] = u / U;
+            wcol[j] = (uint32_t)pb * GB + (uint32_t)(u % U) * 16;
+            wl[j] = (uint32_t)wr[j] * LSTR + (uint32_t)(u % U) * 16;
+        }
+        const int V = ng / SBE;  // scale/bias units per row (ng is a multiple of SBE)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int e = min(64 * j + lane, 16 * V - 1);
+            sr[j] = e / V;
+            scol[j] = e % V;
+        }
+    };
+    set_part(0);
 
     struct StageStd {
         u32x4 w[NI];
@@ -285,10 +304,20 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         }
     };
 
-    // A operands of this part, loaded once: lane (c, i) holds activation row
+    // A operands of the current part: lane (c, i) holds activation row
     // min(i, M-1) (rows past M repeat the last row and are never stored).
+    // Group sums XS[row i][group 4u + c] of the part, as the A operand of one
+    // fp32 MFMA per group quad (the bias term sum_g b[n][g] XS[m][g]).
     half8_t xr[XG][T];
-    {
+    float xsa[Geo::XQ];
+    Stage st[NST];
+    // Start of a pass: the part's activations, the first NST tiles' loads
+    // (issued after the activation loads, so that the loop always finds its
+    // stages in the same order of age), and the part's group sums. Lane block
+    // c sums its quarter of every group with v_dot2 against (1, 1); the
+    // quarters meet in the wave's LDS region (sized for them, and free at the
+    // start of a pass) and are added in lane-block order.
+    auto begin_pass = [&]() {
         const uint16_t *xrow = a.x + (size_t)min(i, M - 1) * K;
 #pragma unroll
         for (int g = 0; g < XG; ++g) {
@@ -300,24 +329,13 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 xr[g][h] = BF16 ? to_pair_order_bf16<BITS>(v) : to_pair_order<BITS>(v);
             }
         }
-    }
-
-    // The first NST tiles' loads, issued after the activation loads so that
-    // the loop always finds its stages in the same order of age.
-    Stage st[NST];
 #pragma unroll
-    for (int k = 0; k < NST; ++k)
-        issue(st[k], t0 + k);
+        for (int k = 0; k < NST; ++k)
+            issue(st[k], t0 + k);
 
-    // Group sums XS[row i][group 4u + c] of this part, as the A operand of
-    // one fp32 MFMA per group quad (the bias term sum_g b'[n][g] XS[m][g]).
-    // Lane block c sums its quarter of every group with v_dot2 against
-    // (1, 1); the quarters meet in the wave's (still unused) LDS region,
-    // sized for them, and are added in lane-block order.
-    float xsa[Geo::XQ];
-    {
         float *xsl = reinterpret_cast<float *>(wmy);
         const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        wave_lds_sync();  // the previous pass's reads of the region are done
 #pragma unroll
         for (int g = 0; g < XG; ++g) {
             float ps = 0.f;
@@ -353,13 +371,14 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         if constexpr (!TILED)
             for (int e = lane; e < 16 * SBSTR; e += kWave)
                 sbmy[e] = 0u;
-    }
+    };
 
     const int chunk_byte = c * (Geo::CHB / 8);
     const int chunk_shift = 8 * (chunk_byte % 4);
     const uint8_t *wrow_lds = wmy + i * LSTR + (chunk_byte & ~3);
     const uint32_t *sbrow = sbmy + i * SBSTR;
 
+    int pass = 0;
     auto process = [&](Stage &sk, int tile) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!TILED) {
@@ -465,7 +484,9 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
         // Partial sums wait in LDS; after every kXrBatch tiles (and the last)
         // one barrier, then wave p sums slot p's KP partials in part order.
         const int lt = tile - t0;
-        const int buf = (lt / kXrBatch) & 1, slot = lt % kXrBatch;
+        // batches are counted across passes, so the two partial-sum buffers
+        // keep alternating at a pass boundary
+        const int buf = (pass * nbatch + lt / kXrBatch) & 1, slot = lt % kXrBatch;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             red_at(buf, slot, kp, r) = acc[r];
@@ -482,8 +503,19 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                     for (int p = 1; p < KP; ++p)
                         v += red_at(buf, sl, p, r);
                     const int m = 4 * c + r;
+                    float o = v * kOutScale;
+                    if constexpr (MP) {
+                        // the running sum of the earlier passes, kept by this thread
+                        float &run = accl[((size_t)(first + sl - t0) * 4 + r) * kWave + lane];
+                        if (pass > 0)
+                            o += run;
+                        if (pass + 1 < npass) {
+                            run = o;
+                            continue;
+                        }
+                    }
                     if (col < N && m < M)
-                        yout[(size_t)m * N + col] = v * kOutScale;
+                        yout[(size_t)m * N + col] = o;
                 }
             }
         }
@@ -495,15 +527,21 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     // NST stages (tiles past the range load one cache line and are not
     // computed), so no path around a stage's loads reaches the back edge and
     // the waits stay per stage.
-    for (int t = t0; t < t1; t += NST) {
+    for (pass = 0; pass < npass; ++pass) {
+        if (pass > 0)
+            set_part(pass);
+        begin_pass();
+        for (int t = t0; t < t1; t += NST) {
 #pragma unroll
-        for (int k = 0; k < NST; ++k)
-            process(st[k], t + k);
+            for (int k = 0; k < NST; ++k)
+                process(st[k], t + k);
+        }
     }
 }
 
 struct XrPlan {
     int KP, gran, sbw;
+    int npass;  // K passes (parts per wave)
 };
 
 // More than 64 KB of dynamic LDS must be allowed per kernel: set the limit
@@ -526,11 +564,35 @@ hipError_t allow_dynamic_lds(const void *const *fns, int count, int bytes, std::
     return hipSuccess;
 }
 
+// Workgroups of a launch: two waves per SIMD fit, so 8 / KP workgroups per
+// CU, shared by the K slices, at most one per tile; multi-pass launches give
+// every workgroup the same number of tiles.
+int xr_grid_x(const ProductArgs &a, int KP, int npass)
+{
+    const int ntiles = (a.N + 15) / 16;
+    const int per_cu = kXrMaxParts / KP;
+    const long long want = ((long long)device_cu_count() * per_cu + a.split - 1) / a.split;
+    int gx = (int)(want < ntiles ? want : ntiles);
+    if (npass > 1) {
+        const int per = (ntiles + gx - 1) / gx;
+        gx = (ntiles + per - 1) / per;
+    }
+    return gx;
+}
+
+// Multi-pass launches keep each tile's running sum (4 x 64 floats) in LDS
+// between passes.
+size_t xr_run_bytes(const ProductArgs &a, int gx, int npass)
+{
+    const int ntiles = (a.N + 15) / 16;
+    return npass > 1 ? (size_t)((ntiles + gx - 1) / gx) * 4 * kWave * sizeof(float) : 0;
+}
+
 // The register-resident kernel needs: whole 16-byte rows of packed codes,
 // K slices starting on a granule, at most kXrMaxParts parts of at most
 // XC activations each, and no empty part.
 template <int BITS, int G, int XC>
-bool plan_xr(const ProductArgs &a, XrPlan &plan)
+bool plan_xr(const ProductArgs &a, XrPlan &plan, int max_pass = 1)
 {
     using Geo = XrGeo<BITS, G, XC>;
     const int Kg = a.K / G;
@@ -552,54 +614,22 @@ bool plan_xr(const ProductArgs &a, XrPlan &plan)
     if (per_part < 1)
         return false;
     const int nu_max = (lmax + gran - 1) / gran, nu_min = (lmin + gran - 1) / gran;
-    const int KP = (nu_max + per_part - 1) / per_part;
-    if (KP > kXrMaxParts || KP > nu_min)
+    // parts of at most per_part granules: KP waves, each walking npass of them
+    const int parts = (nu_max + per_part - 1) / per_part;
+    const int npass = (parts + kXrMaxParts - 1) / kXrMaxParts;
+    if (npass > max_pass)
+        return false;
+    const int KP = (parts + npass - 1) / npass;
+    const int total = KP * npass;
+    if (total > nu_min)
         return false;
     // a part whose granule count is at its maximum must still fit
-    if (((nu_max + KP - 1) / KP) * gran > Geo::XG)
+    if (((nu_max + total - 1) / total) * gran > Geo::XG)
         return false;
-    plan = XrPlan{KP, gran, sbw};
+    if (npass > 1 && xr_lds_bytes<BITS, G, XC>(KP) + xr_run_bytes(a, xr_grid_x(a, KP, npass), npass) > kXrLdsLimit)
+        return false;
+    plan = XrPlan{KP, gran, sbw, npass};
     return true;
-}
-
-template <int BITS, int G, int XC, bool BF16>
-hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
-{
-    XrArgs xa{a, plan.gran, (a.N + 15) / 16};
-    // two waves per SIMD fit: 8 / KP workgroups per CU
-    const int per_cu = kXrMaxParts / plan.KP;
-    long long want = ((long long)device_cu_count() * per_cu + a.split - 1) / a.split;
-    const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
-    const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
-    const size_t lds = xr_lds_bytes<BITS, G, XC>(plan.KP);
-    constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
-    // bf16 launches are single-projection only (no fused bf16 entry point)
-    const bool fused = !BF16 && a.nproj >= 2;
-    // more than 64 KB of dynamic LDS must be allowed per kernel, once
-    static std::atomic<uint64_t> allowed{0};
-    {
-        const int cap = (int)xr_lds_bytes<BITS, G, XC>(kXrMaxParts);
-        const void *fns[4] = {
-            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>),
-            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>),
-            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>),
-            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>)};
-        const hipError_t e = allow_dynamic_lds(fns, 4, cap, allowed);
-        if (e != hipSuccess)
-            return e;
-    }
-    if (plan.sbw == 4) {
-        if (fused)
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>), grid, block, lds, stream, xa);
-        else
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>), grid, block, lds, stream, xa);
-    } else {
-        if (fused)
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>), grid, block, lds, stream, xa);
-        else
-            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>), grid, block, lds, stream, xa);
-    }
-    return hipGetLastError();
 }
 
 // Variants of a width, preferred first: fewer activation registers leave
@@ -615,6 +645,78 @@ template <int BITS>
 constexpr int xr_tiled_small_codes() { return BITS == 8 ? 512 : 640; }
 template <int BITS>
 constexpr int xr_tiled_large_codes() { return BITS == 8 ? 512 : 768; }
+#ifndef XR_MP_WIDE
+#define XR_MP_WIDE 1
+#endif
+// Parts of the multi-pass variants (several K parts per wave).
+template <int BITS>
+constexpr int xr_pass_codes() { return XR_MP_WIDE && BITS <= 4 ? xr_large_codes<BITS>() : xr_small_codes<BITS>(); }
+
+template <int BITS, int G, int XC, bool BF16>
+hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
+{
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16, plan.npass};
+    const int gx = xr_grid_x(a, plan.KP, plan.npass);
+    const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
+    const size_t lds = xr_lds_bytes<BITS, G, XC>(plan.KP) + xr_run_bytes(a, gx, plan.npass);
+    if (lds > kXrLdsLimit)  // excluded by plan_xr
+        return hipErrorInvalidValue;
+    constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
+    // bf16 launches are single-projection only (no fused bf16 entry point)
+    const bool fused = !BF16 && a.nproj >= 2;
+    // more than 64 KB of dynamic LDS must be allowed per kernel, once
+    static std::atomic<uint64_t> allowed{0};
+    {
+        const int cap = (int)kXrLdsLimit;
+        constexpr bool kMP = XC == xr_pass_codes<BITS>();  // multi-pass variants exist for one width only
+        const void *fns[8] = {
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16, kMP>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16, kMP>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16, kMP>),
+            reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16, kMP>)};
+        const hipError_t e = allow_dynamic_lds(fns, 8, cap, allowed);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (plan.npass > 1) {  // multi-pass plans take the narrow parts (plan_xr_any)
+        if constexpr (XC == xr_pass_codes<BITS>()) {
+            if (plan.sbw == 4) {
+                if (fused)
+                    hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16, true>), grid, block,
+                                       lds, stream, xa);
+                else
+                    hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16, true>), grid, block,
+                                       lds, stream, xa);
+            } else {
+                if (fused)
+                    hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16, true>), grid, block,
+                                       lds, stream, xa);
+                else
+                    hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16, true>), grid, block,
+                                       lds, stream, xa);
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (plan.sbw == 4) {
+        if (fused)
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, !BF16, false, BF16>), grid, block, lds, stream, xa);
+        else
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 4, NST4, false, false, BF16>), grid, block, lds, stream, xa);
+    } else {
+        if (fused)
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, !BF16, false, BF16>), grid, block, lds, stream, xa);
+        else
+            hipLaunchKernelGGL((mfma_xr_kernel<BITS, G, XC, 2, NST2, false, false, BF16>), grid, block, lds, stream, xa);
+    }
+    return hipGetLastError();
+}
+
 
 template <int BITS, int G>
 bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
@@ -625,6 +727,11 @@ bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
     }
     if (plan_xr<BITS, G, xr_large_codes<BITS>()>(a, plan)) {
         xc = xr_large_codes<BITS>();
+        return true;
+    }
+    // K too long for one pass: the narrow parts, several per wave
+    if (plan_xr<BITS, G, xr_pass_codes<BITS>()>(a, plan, kXrMaxPasses)) {
+        xc = xr_pass_codes<BITS>();
         return true;
     }
     return false;
@@ -742,7 +849,7 @@ bool plan_xr_tiled(const ProductArgs &a, XrPlan &plan)
     const int KP = (nu + per_part - 1) / per_part;
     if (KP > kXrMaxParts || KP > nu || ((nu + KP - 1) / KP) * gran > Geo::XG)
         return false;
-    plan = XrPlan{KP, gran, 4};
+    plan = XrPlan{KP, gran, 4, 1};
     return true;
 }
 
@@ -762,7 +869,7 @@ constexpr int xr_tiled_stages()
 template <int BITS, int G, int XC>
 hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
-    XrArgs xa{a, plan.gran, (a.N + 15) / 16};
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16, 1};
     const int per_cu = kXrMaxParts / plan.KP;
     const long long want = (long long)device_cu_count() * per_cu;
     const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);

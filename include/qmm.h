@@ -315,9 +315,11 @@ const char *qmm_kernel_name(int M, int K, int N, int bits, int G);
  *              rows per launch; qmm_forward's choice for M <= 2;
  *   "mfma"     the multi-row matrix-core kernel with each wave's K part of
  *              the activations in registers; qmm_forward's choice for M >= 3
- *              when the shape allows it (K * bits a multiple of 128 and K
- *              short enough for 8 parts of 768 activations, 640 for 8-bit
- *              codes); QMM_ERR_UNSUPPORTED otherwise;
+ *              when the shape allows it (K * bits a multiple of 128, and K
+ *              within 8 parts of 768 activations (640 for 8-bit codes) or,
+ *              for longer K, within 8 passes of 8 parts of 640, each wave
+ *              walking its parts one after the other); QMM_ERR_UNSUPPORTED
+ *              otherwise;
  *   "mfma_lds" the multi-row matrix-core kernel that streams activations
  *              through LDS; any shape except 3-bit codes at G = 32
  *              (QMM_ERR_UNSUPPORTED); qmm_forward's choice for M >= 3 when

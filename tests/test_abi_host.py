@@ -84,24 +84,28 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(3, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 7, 32) is None
-    # activations of K = 17408 do not fit 8 parts of 768: the LDS-streaming kernel
-    assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma_lds"
+    # K past 8 parts of 768 activations: each wave walks several parts of 640
+    # (at most 8 per wave), past that the LDS-streaming kernel
+    assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(4, 6144, 1024, 4, 32) == "mfma"
-    assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma"
+    assert qmm.qmm_kernel_name(4, 40960, 64, 4, 32) == "mfma"      # 8 passes of 8 parts of 640
+    assert qmm.qmm_kernel_name(4, 49152, 64, 4, 32) == "mfma_lds"  # would take 10 passes
     assert qmm.qmm_kernel_name(4, 65536, 64, 4, 32) == "mfma_lds"
     # 5-bit rows of 13 groups are not whole 16-byte units
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 8, 64) == "mfma"      # 8-bit: parts of 640 activations
-    assert qmm.qmm_kernel_name(4, 17408, 5120, 8, 64) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 17408, 5120, 8, 64) == "mfma"
     assert qmm.qmm_kernel_name(4, 5120, 5120, 6, 64) == "mfma"
     # 2- and 3-bit codes
     assert qmm.qmm_kernel_name(2, 5120, 1000, 2, 32) == "qmv"
     assert qmm.qmm_kernel_name(8, 5120, 1000, 2, 32) == "mfma"
     assert qmm.qmm_kernel_name(8, 5120, 1000, 3, 32) == "mfma"
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 2, 32) == "mfma"
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 64) == "mfma"
+    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 32) == "mfma"
     # past the register-resident kernel: LDS kernel, except 3-bit G=32 (VALU kernel)
-    assert qmm.qmm_kernel_name(8, 17408, 1000, 2, 32) == "mfma_lds"
-    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 64) == "mfma_lds"
-    assert qmm.qmm_kernel_name(8, 17408, 1000, 3, 32) == "qmv"
+    assert qmm.qmm_kernel_name(8, 65536, 1000, 2, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(8, 65536, 1000, 3, 32) == "qmv"
 
 

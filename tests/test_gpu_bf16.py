@@ -87,13 +87,14 @@ def test_bf16_rejects_fp16_tensors():
 
 @pytest.mark.parametrize("bits,G,K,M,kernel", [
     (4, 32, 5120, 5, "mfma"),         # register-resident kernel
-    (4, 32, 17408, 5, "mfma_lds"),    # activations past the register-resident kernel: LDS-streaming kernel
+    (4, 32, 17408, 5, "mfma"),        # several K parts per wave (4 passes)
     (8, 64, 5120, 8, "mfma"),
-    (8, 64, 17408, 8, "mfma_lds"),
-    (5, 32, 13 * 32, 4, "mfma_lds"),  # rows not whole 16-byte units
-    (4, 32, 65536, 3, "mfma_lds"),
-    (3, 32, 17408, 16, "qmv"),        # neither matrix-core kernel: the VALU kernel
-    (3, 32, 65536, 3, "qmv"),
+    (8, 64, 17408, 8, "mfma"),
+    (3, 32, 17408, 16, "mfma"),
+    (5, 32, 13 * 32, 4, "mfma_lds"),  # rows not whole 16-byte units: LDS-streaming kernel
+    (4, 32, 65536, 3, "mfma_lds"),    # more than 8 passes
+    (8, 64, 65536, 8, "mfma_lds"),
+    (3, 32, 65536, 3, "qmv"),         # neither matrix-core kernel: the VALU kernel
     (6, 64, 5120, 16, "mfma"),
 ])
 def test_bf16_each_kernel_path(bits, G, K, M, kernel):

@@ -26,7 +26,8 @@ def make_projections(seed, M, K, Ns, bits, G):
     (6, 32, 1280, [17, 1]),
     (8, 128, 2048, [64, 40, 24]),
     (4, 32, 5632, [40, 72]),              # 768-activation parts of the multi-row kernel
-    (4, 32, 17408, [33, 20]),             # past the register-resident kernel: LDS kernel
+    (4, 32, 17408, [33, 20]),             # several K parts per wave
+    (4, 32, 65536, [33, 20]),             # more than 8 passes: LDS kernel
     (5, 32, 416, [40, 9]),                # rows not whole 16-byte units: LDS kernel
 ])
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 16, 19])
