@@ -84,13 +84,16 @@ def test_kernel_choice():
     assert qmm.qmm_kernel_name(3, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(16, 5120, 17408, 7, 32) is None
-    # K past 8 parts of 768 activations: each wave walks several parts of 640
-    # (at most 8 per wave), past that the LDS-streaming kernel
+    # K past 8 parts of 768 activations: each wave walks several parts (768
+    # activations for 2-4-bit codes, 640 otherwise; at most 8 passes), past
+    # that the LDS-streaming kernel
     assert qmm.qmm_kernel_name(16, 17408, 5120, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(4, 6144, 1024, 4, 32) == "mfma"
     assert qmm.qmm_kernel_name(4, 6176, 1024, 4, 32) == "mfma"
-    assert qmm.qmm_kernel_name(4, 40960, 64, 4, 32) == "mfma"      # 8 passes of 8 parts of 640
-    assert qmm.qmm_kernel_name(4, 49152, 64, 4, 32) == "mfma_lds"  # would take 10 passes
+    assert qmm.qmm_kernel_name(4, 49152, 64, 4, 32) == "mfma"      # 8 passes of 8 parts of 768
+    assert qmm.qmm_kernel_name(4, 49152 + 64, 64, 4, 32) == "mfma_lds"
+    assert qmm.qmm_kernel_name(4, 40960, 64, 8, 32) == "mfma"      # 8 passes of 8 parts of 640
+    assert qmm.qmm_kernel_name(4, 40960 + 64, 64, 8, 32) == "mfma_lds"
     assert qmm.qmm_kernel_name(4, 65536, 64, 4, 32) == "mfma_lds"
     # 5-bit rows of 13 groups are not whole 16-byte units
     assert qmm.qmm_kernel_name(4, 13 * 32, 200, 5, 32) == "mfma_lds"
