@@ -333,7 +333,7 @@ def qmm_stream_read_sink_words(nbytes: int) -> int:
 
 def qmm_stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
     """Streaming-read ceiling: reads every byte of the contiguous GPU tensor
-    `src` once; returns the int32 sink (one XOR word per 64 KiB span)."""
+    `src` once; returns the int32 sink (one XOR word per 8 KiB span)."""
     if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
         raise ValueError("src must be a contiguous GPU tensor")
     nbytes = src.numel() * src.element_size()

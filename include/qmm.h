@@ -334,8 +334,8 @@ int qmm_forward_kernel(const char *kernel, const uint16_t *x, const uint32_t *wq
  * the `bytes` bytes at `src` once, with the 16-byte non-temporal loads the
  * product kernels use for packed codes, every load of a thread issued before
  * any is used, and writes one word per workgroup to `sink`: the XOR of the
- * 32-bit words that workgroup read (workgroup w reads the 64 KiB span
- * starting at byte w * 65536; the last span may be short). Its time bounds
+ * 32-bit words that workgroup read (workgroup w reads the 8 KiB span
+ * starting at byte w * 8192; the last span may be short). Its time bounds
  * what any kernel that must read those bytes can reach on this GPU, which is
  * how the one-row product's weight stream is judged (it reads each weight
  * byte once and writes almost nothing).

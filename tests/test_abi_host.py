@@ -152,8 +152,8 @@ def test_stream_read_rejects_before_launch():
     assert qmm.qmm_stream_read_sink_words(0) == 0
     assert qmm.qmm_stream_read_sink_words(40) == 0
     assert qmm.qmm_stream_read_sink_words(16) == 1
-    assert qmm.qmm_stream_read_sink_words(65536) == 1
-    assert qmm.qmm_stream_read_sink_words(65536 + 16) == 2
+    assert qmm.qmm_stream_read_sink_words(8192) == 1
+    assert qmm.qmm_stream_read_sink_words(8192 + 16) == 2
     assert lib.qmm_stream_read(None, 64, A, None) == -1
     assert lib.qmm_stream_read(A, 64, None, None) == -1
     assert lib.qmm_stream_read(A, 0, A, None) == -2
