@@ -343,8 +343,13 @@ hipError_t launch_qmv_upto(const ProductArgs &a, int slots, hipStream_t stream)
     // PD: with 32 lanes per row both row groups of a wave stay in flight
     // (measured: 12.7 us against 13.8 us with one on the 5120 x 17408 4-bit
     // projection at M = 1).
-    constexpr int PDR = LPR == 32 ? 2 : kPrefetchRows;
-    constexpr int RPW = MR <= 2 ? kWave / LPR : kRowsPerWave;
+    // Two-row launches with 32 lanes per row take two row groups per wave,
+    // one in flight at a time (half the workgroups, the same registers):
+    // 15.9-16.4 us against 16.5-17.5 us on the 5120 x 17408 4-bit projection
+    // (the one-row launch is faster with one row group per wave).
+    constexpr bool kTwoGroups = MR == 2 && LPR == 32;
+    constexpr int PDR = kTwoGroups ? 1 : LPR == 32 ? 2 : kPrefetchRows;
+    constexpr int RPW = kTwoGroups ? 4 : MR <= 2 ? kWave / LPR : kRowsPerWave;
     if constexpr (S > 1) {
         if (slots < S)
             return launch_qmv_upto<BITS, G, LPR, MR, S - 1, BF16>(a, slots, stream);
