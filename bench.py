@@ -53,6 +53,9 @@ the counters. Helper modes (used with rocprofv3, see profiles/):
   --summarize-dispatches T DIR --manifest M   kernel-trace CSV directory of a
                             profile run -> per-label durations, one summary
                             per set under DIR;
+  --summarize-counters D1 .. Dn DIR --manifest M   any counters of profile
+                            runs (e.g. the SQ instruction and cycle counts)
+                            -> one summary per set under DIR;
   --summarize-trace D OUT   kernel-trace stats directory of a bench run ->
                             text summary OUT.
 """
@@ -129,6 +132,8 @@ def parse(argv=None):
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_DIR"))
     ap.add_argument("--summarize-dispatches", nargs=2, metavar=("TRACE_DIR", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="counter CSV directories of profile runs, then the output directory")
     return ap.parse_args(argv)
 
 
@@ -305,6 +310,50 @@ def summarize_dispatches(trace_dir: str, out_dir: str, manifest_path: str):
             kind = kernel_short(c["kernel"]) or "other"
             lines.append(f"{label} | {kind}: {c['kernel'][:110]} | {len(us)} | {avg:.3f} | {min(us):.3f} | "
                          f"{max(us):.3f} | {c['algo']} | {rate:.1f} | {100 * rate / HBM_PEAK_GBPS:.2f}")
+        out.write_text("\n".join(lines) + "\n")
+        written.append(out)
+        print("\n".join(lines))
+    return written
+
+
+def summarize_counters(dirs, out_dir: str, manifest_path: str):
+    """Any rocprofv3 counters of profile runs (one or more counter CSV
+    directories, each a run of the same manifest) -> per-label averages, one
+    summary per profile set under out_dir ("<stem>_sq_counters.txt")."""
+    manifest = json.loads(Path(manifest_path).read_text())
+    table = {}  # (set, label) -> {"kernel": name, counter: [values]}
+    names = []
+    for d in dirs:
+        rows = _csv_rows(d, "counter_collection.csv")
+        counters = sorted({r["Counter_Name"] for r in rows})
+        for c in counters:
+            if c not in names:
+                names.append(c)
+            pairs, _ = _split_library(_per_dispatch(d, c), manifest)
+            for lab, (kname, v) in pairs:
+                if lab["round"] == 0:  # cold caches
+                    continue
+                e = table.setdefault((lab["set"], lab["label"]), {"kernel": kname})
+                e.setdefault(c, []).append(v)
+    written = []
+    for set_name in manifest["sets"]:
+        out = Path(out_dir) / f"{SET_FILES[set_name]}_sq_counters.txt"
+        lines = [
+            f"# rocprofv3 SQ counters per dispatch (averages over warm rounds), profile set '{set_name}' "
+            f"({manifest['workloads'][set_name]})",
+            "# commands (from the repository root on the GPU host), one run per counter group:",
+            f"#   rocprofv3 --pmc <counters> --output-format csv -d <D_i> -o run -- python3 bench.py "
+            f"--profile-run {manifest['run']} --manifest <MAN>",
+            f"#   python3 bench.py --summarize-counters <D_1> ... <D_n> {_repo_relative(out_dir)} --manifest <MAN>",
+            "# SQ_INSTS_* count wave instructions; *_CYCLES are summed over the counter instances",
+            "label | kernel | " + " | ".join(names),
+        ]
+        for (s_, label), e in table.items():
+            if s_ != set_name:
+                continue
+            kind = kernel_short(e["kernel"]) or "other"
+            vals = [f"{sum(e[c]) / len(e[c]):.0f}" if c in e else "-" for c in names]
+            lines.append(f"{label} | {kind} | " + " | ".join(vals))
         out.write_text("\n".join(lines) + "\n")
         written.append(out)
         print("\n".join(lines))
@@ -1001,6 +1050,9 @@ def main(argv=None):
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], args.manifest)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the product shards along N "

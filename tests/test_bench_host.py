@@ -121,3 +121,18 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU only" in capsys.readouterr().err
+
+
+def test_counter_summary_averages_warm_rounds(tmp_path):
+    rows, manifest = _profile_run("SQ_INSTS_VALU", {1: 100.0, 4: 400.0, 16: 1600.0, "copy": 1.0}.__getitem__)
+    # the cold first round reads differently and must be dropped
+    rows = [(d, n, c, (v * 3 if d < 3 + len(bench.CELLS_M) and "qmm::" in n else v)) for d, n, c, v in rows]
+    _write_counters(tmp_path / "a", rows)
+    man = tmp_path / "manifest.json"
+    man.write_text(json.dumps(manifest))
+    out = tmp_path / "out"
+    out.mkdir()
+    written = bench.summarize_counters([str(tmp_path / "a")], str(out), str(man))
+    text = written[0].read_text()
+    assert written[0].name == "dense_up_w4g32_sq_counters.txt"
+    assert "M1 | qmv | 100" in text and "M4 | mfma | 400" in text and "M16 | mfma | 1600" in text
