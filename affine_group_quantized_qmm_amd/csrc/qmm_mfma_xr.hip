@@ -17,10 +17,14 @@
 //
 // Work split. A workgroup of KP waves walks a contiguous range of 16-row
 // tiles. Wave kp owns the kp-th of KP parts of the K range (at most 768
-// activations per row, 512 for 8-bit codes) and loads its A operands once,
+// activations per row, 640 for 8-bit codes) and loads its A operands once,
 // into registers, for the whole launch. The KP partial tiles wait in LDS
 // and are summed in a fixed part order after every batch of tiles (one
-// barrier per batch), so results do not depend on timing.
+// barrier per batch), so results do not depend on timing. When K does not
+// fit KP parts, each wave walks several parts in turn (passes): at each pass
+// it reloads its activations and group sums and streams the workgroup's
+// tiles again over the next K range, and each tile's running sum waits in
+// LDS until the last pass writes y.
 //
 // Weights. Every lane of a 16-byte load reads a consecutive piece of one
 // weight row, so one load instruction covers whole row segments (the 16 rows
@@ -28,8 +32,8 @@
 // streams from HBM at full rate. The wave writes the block to its own LDS
 // region and reads back each lane's chunk in the MFMA B layout; the tile's
 // scales and biases go the same way, interleaved as (s | b << 16) words. The
-// loads of the tile NST ahead are issued as soon as the current one is in
-// LDS, so they stream while NST tiles are computed.
+// loads of the tile NST ahead (one register stage) are issued as soon as the
+// current one is in LDS, so they stream while it is computed.
 #include <atomic>
 
 #include "qmm_device.hpp"
