@@ -50,7 +50,7 @@ constexpr size_t kXrLdsLimit = 160 * 1024;  // LDS of one CU
 #define XR_MAX_PASSES 8
 #endif
 constexpr int kXrMaxPasses = XR_MAX_PASSES;  // K parts per wave (activations reloaded between them)
-constexpr int kXrBatch = 4;       // tiles whose partial sums are reduced after one barrier
+constexpr int kXrBatchMax = 6;    // tiles whose partial sums are reduced after one barrier, at most
 
 // Activations per row held by one wave (XC: 640 or 768, 512 for 8-bit codes,
 // i.e. 80 to 96 registers of A operands). The host takes the first variant
@@ -99,6 +99,8 @@ struct XrArgs {
     int gran;    // part boundary granularity in groups
     int ntiles;  // 16-row tiles of N
     int npass;   // K passes: wave kp owns parts kp, KP + kp, 2 KP + kp, ... of the slice
+    int batch;   // tiles whose partial sums are reduced after one barrier
+    int nbuf;    // partial-sum buffers: 1 when one batch holds every tile of a workgroup's one pass, else 2
 };
 
 // Group range [pb, pe) of part kp: the slice [gb, ge) cut into KP parts of
@@ -114,8 +116,8 @@ __device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int g
 
 // Dynamic LDS of one workgroup of KP waves: per wave a weight tile region
 // (16 x LSTR bytes) and a scale/bias region (16 x SBSTR words), at least as
-// large as the group-sum scratch of the start (XG x 64 floats), then two
-// buffers of kXrBatch tiles of partial sums.
+// large as the group-sum scratch of the start (XG x 64 floats), then `nbuf`
+// buffers of `batch` tiles of partial sums (XrArgs).
 // (The tiled-layout variant keeps its weights in registers: only the group-
 // sum scratch.)
 template <int BITS, int G, int XC, bool TILED = false>
@@ -127,9 +129,9 @@ __host__ __device__ constexpr size_t xr_wave_lds()
     return run > xs ? run : xs;
 }
 template <int BITS, int G, int XC, bool TILED = false>
-__host__ __device__ constexpr size_t xr_lds_bytes(int KP)
+__host__ __device__ constexpr size_t xr_lds_bytes(int KP, int batch, int nbuf)
 {
-    return (size_t)KP * xr_wave_lds<BITS, G, XC, TILED>() + 2 * (size_t)kXrBatch * KP * 4 * kWave * sizeof(float);
+    return (size_t)KP * xr_wave_lds<BITS, G, XC, TILED>() + (size_t)nbuf * batch * KP * 4 * kWave * sizeof(float);
 }
 
 // Tiled (MFMA-native) layout, for codes whose lane chunk (the G/4 codes lane
@@ -178,11 +180,11 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     // red[buf][slot][part][r][lane]
     float *const red = reinterpret_cast<float *>(xr_lds + (size_t)KP * xr_wave_lds<BITS, G, XC, TILED>());
     auto red_at = [&](int buf, int slot, int part, int r) -> float & {
-        return red[(((size_t)(buf * kXrBatch + slot) * KP + part) * 4 + r) * kWave + lane];
+        return red[(((size_t)(buf * xa.batch + slot) * KP + part) * 4 + r) * kWave + lane];
     };
     // multi-pass: the running sums of the workgroup's tiles between passes,
     // accl[tile - t0][r][lane], each word read and written by one thread only
-    float *const accl = red + 2 * (size_t)kXrBatch * KP * 4 * kWave;
+    float *const accl = red + (size_t)xa.nbuf * xa.batch * KP * 4 * kWave;
     const int c = lane / 16, i = lane % 16;
     const int M = a.M, K = a.K, Kg = K / G;
     // projection of a tile; single-projection launches skip the lookup
@@ -202,7 +204,8 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
     // tiles of this workgroup
     const int t0 = (int)(((long long)blockIdx.x * xa.ntiles) / gridDim.x);
     const int t1 = (int)(((long long)(blockIdx.x + 1) * xa.ntiles) / gridDim.x);
-    const int nbatch = (t1 - t0 + kXrBatch - 1) / kXrBatch;  // barriers per pass
+    const int batch = xa.batch;
+    const int nbatch = (t1 - t0 + batch - 1) / batch;  // barriers per pass
 
     // This wave's K part of the current pass, [pb, pe) (ng >= 1: the host never
     // makes empty parts), and the per-lane load geometry of that part. Weight
@@ -485,16 +488,16 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 }
             }
         }
-        // Partial sums wait in LDS; after every kXrBatch tiles (and the last)
+        // Partial sums wait in LDS; after every `batch` tiles (and the last)
         // one barrier, then wave p sums slot p's KP partials in part order.
         const int lt = tile - t0;
         // batches are counted across passes, so the two partial-sum buffers
         // keep alternating at a pass boundary
-        const int buf = (pass * nbatch + lt / kXrBatch) & 1, slot = lt % kXrBatch;
+        const int buf = (pass * nbatch + lt / batch) & (xa.nbuf - 1), slot = lt % batch;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             red_at(buf, slot, kp, r) = acc[r];
-        if (slot == kXrBatch - 1 || tile == t1 - 1) {  // uniform over the workgroup
+        if (slot == batch - 1 || tile == t1 - 1) {  // uniform over the workgroup
             __syncthreads();
             const int first = tile - slot;
             for (int sl = kp; sl <= slot; sl += KP) {
@@ -584,12 +587,33 @@ int xr_grid_x(const ProductArgs &a, int KP, int npass)
     return (ntiles + per - 1) / per;
 }
 
-// Multi-pass launches keep each tile's running sum (4 x 64 floats) in LDS
-// between passes.
-size_t xr_run_bytes(const ProductArgs &a, int gx, int npass)
+// Grid, barrier batch and LDS of a launch: one batch holds every tile of a
+// workgroup's pass when that fits (one barrier per pass, and a single
+// partial-sum buffer when there is one pass), else batches of up to
+// kXrBatchMax tiles in two alternating buffers, smaller while the LDS does
+// not fit. Multi-pass launches also keep each tile's running sum (4 x 64
+// floats) in LDS between passes. Measured on the 5120 x 17408 projection
+// (218 workgroups of 5 tiles): 19.8-20.1 us at M = 16 with one barrier per
+// workgroup against 20.6-21.3 with barriers after every 4 tiles.
+struct XrShape {
+    int gx, batch, nbuf;
+    size_t lds;
+};
+template <int BITS, int G, int XC, bool TILED = false>
+bool xr_shape(const ProductArgs &a, int KP, int npass, int gx, XrShape &sh)
 {
     const int ntiles = (a.N + 15) / 16;
-    return npass > 1 ? (size_t)((ntiles + gx - 1) / gx) * 4 * kWave * sizeof(float) : 0;
+    const int tpw = (ntiles + gx - 1) / gx;
+    const size_t run = npass > 1 ? (size_t)tpw * 4 * kWave * sizeof(float) : 0;
+    for (int b = tpw < kXrBatchMax ? tpw : kXrBatchMax; b >= 1; --b) {
+        const int nbuf = npass == 1 && tpw <= b ? 1 : 2;
+        const size_t lds = xr_lds_bytes<BITS, G, XC, TILED>(KP, b, nbuf) + run;
+        if (lds <= kXrLdsLimit) {
+            sh = XrShape{gx, b, nbuf, lds};
+            return true;
+        }
+    }
+    return false;
 }
 
 // The register-resident kernel needs: whole 16-byte rows of packed codes,
@@ -630,7 +654,8 @@ bool plan_xr(const ProductArgs &a, XrPlan &plan, int max_pass = 1)
     // a part whose granule count is at its maximum must still fit
     if (((nu_max + total - 1) / total) * gran > Geo::XG)
         return false;
-    if (npass > 1 && xr_lds_bytes<BITS, G, XC>(KP) + xr_run_bytes(a, xr_grid_x(a, KP, npass), npass) > kXrLdsLimit)
+    XrShape sh;
+    if (!xr_shape<BITS, G, XC>(a, KP, npass, xr_grid_x(a, KP, npass), sh))
         return false;
     plan = XrPlan{KP, gran, sbw, npass};
     return true;
@@ -659,12 +684,12 @@ constexpr int xr_pass_codes() { return XR_MP_WIDE && BITS <= 4 ? xr_large_codes<
 template <int BITS, int G, int XC, bool BF16>
 hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
-    XrArgs xa{a, plan.gran, (a.N + 15) / 16, plan.npass};
-    const int gx = xr_grid_x(a, plan.KP, plan.npass);
-    const dim3 grid(gx, 1, a.split), block(plan.KP * kWave);
-    const size_t lds = xr_lds_bytes<BITS, G, XC>(plan.KP) + xr_run_bytes(a, gx, plan.npass);
-    if (lds > kXrLdsLimit)  // excluded by plan_xr
-        return hipErrorInvalidValue;
+    XrShape sh;
+    if (!xr_shape<BITS, G, XC>(a, plan.KP, plan.npass, xr_grid_x(a, plan.KP, plan.npass), sh))
+        return hipErrorInvalidValue;  // excluded by plan_xr
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16, plan.npass, sh.batch, sh.nbuf};
+    const dim3 grid(sh.gx, 1, a.split), block(plan.KP * kWave);
+    const size_t lds = sh.lds;
     constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
     // bf16 launches are single-projection only (no fused bf16 entry point)
     const bool fused = !BF16 && a.nproj >= 2;
@@ -873,16 +898,20 @@ constexpr int xr_tiled_stages()
 template <int BITS, int G, int XC>
 hipError_t launch_xr_tiled_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
 {
-    XrArgs xa{a, plan.gran, (a.N + 15) / 16, 1};
+    const int ntiles = (a.N + 15) / 16;
     const int per_cu = kXrMaxParts / plan.KP;
     const long long want = (long long)device_cu_count() * per_cu;
-    const int gx = (int)(want < xa.ntiles ? want : xa.ntiles);
-    const size_t lds = xr_lds_bytes<BITS, G, XC, true>(plan.KP);
+    const int gx = (int)(want < ntiles ? want : ntiles);
+    XrShape sh;
+    if (!xr_shape<BITS, G, XC, true>(a, plan.KP, 1, gx, sh))
+        return hipErrorInvalidValue;
+    XrArgs xa{a, plan.gran, ntiles, 1, sh.batch, sh.nbuf};
+    const size_t lds = sh.lds;
     constexpr int NST = xr_tiled_stages<BITS, G, XC>();
     static std::atomic<uint64_t> allowed{0};
     {
         const void *fns[1] = {reinterpret_cast<const void *>(&mfma_xr_kernel<BITS, G, XC, 4, NST, false, true>)};
-        const hipError_t e = allow_dynamic_lds(fns, 1, (int)xr_lds_bytes<BITS, G, XC, true>(kXrMaxParts), allowed);
+        const hipError_t e = allow_dynamic_lds(fns, 1, (int)kXrLdsLimit, allowed);
         if (e != hipSuccess)
             return e;
     }
