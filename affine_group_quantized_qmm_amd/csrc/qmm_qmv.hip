@@ -45,7 +45,15 @@ constexpr int chunk_limit(int mr) { return mr == 1 ? kMaxChunkK : 2 * kMaxChunkK
 // an MR-row result is bitwise equal to that row computed alone.
 // BF16: x, scales and biases hold bf16 bit patterns (codes widened to bf16
 // and dotted with v_dot2_f32_bf16) instead of fp16.
-template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR, bool BF16>
+// WS: coalesced weight loads for groups wider than 16 bytes. A lane that
+// loads its own group's bytes reads 16-byte pieces at the group stride, and
+// such loads stream at about half the rate of contiguous ones (measured on
+// the 5120 x 5120 8-bit G = 64 matrix with this kernel's grid: 9.5 against
+// 5.3 us). With WS the lanes of a row load consecutive 16-byte pieces of the
+// slot's span, write them to the wave's LDS region and read back their own
+// group's words: the same words reach the same lane, so the results keep
+// their bits. Needs 16-byte aligned rows and one K slice (the host checks).
+template <int BITS, int G, int LPR, int SLOTS, int RPW, int PD_ROWS, int MR, bool BF16, bool WS = false>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
 {
     constexpr int NWG = G * BITS / 32;        // words per group
@@ -65,12 +73,24 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
     constexpr int SPT = (SBU + kThreads - 1) / kThreads;            // ... per thread
     static_assert(MR * CHUNK_G * G <= chunk_limit(MR), "staged chunk too large");
     static_assert(CHUNK_G % 8 == 0, "chunks hold whole 8-group scale units");
+    // WS geometry: 16-byte pieces per lane and task; a row's region holds the
+    // slot's LPR groups, each padded to an odd number of 16-byte units when
+    // whole units hold a group (so that lanes reading their groups spread over
+    // the LDS banks)
+    constexpr int GBY = 4 * NWG;                                   // bytes per group
+    constexpr int NPC = (GBY + 15) / 16;
+    constexpr int GU = GBY % 16 == 0 ? GBY / 16 : 0;               // whole units per group
+    constexpr int GSTRIDE = GU ? 16 * (GU | 1) : GBY;              // region bytes per group
+    constexpr int RUNITS = GU ? LPR * (GU | 1) : LPR * NPC;        // region units per row
+    constexpr int RALIGN = gcd_int(GSTRIDE, 16);                   // alignment of a group in the region
+    static_assert(!WS || GBY > 16, "coalesced loads are for groups wider than 16 bytes");
 
     // Activations unit-major: xp[m][u][g] holds unit u of group g of row m,
     // so the lanes of a row (consecutive groups) read consecutive 16-byte units.
     __shared__ half8_t xp[MR][UPG][CHUNK_G];
     __shared__ float xsum[MR][CHUNK_G];
     __shared__ uint32_t sbl[ROWS][CHUNK_G];   // (scale, bias) fp16 pair per row and group
+    __shared__ u32x4 wst[WS ? kWaves * RPI * RUNITS : 1];  // WS: per wave, RPI rows of a slot's pieces
 
     static_assert(16 % ROWS == 0, "a workgroup owns a whole part of one 16-row tile");
     constexpr int TPW = 16 / ROWS;                     // workgroups per 16-row tile
@@ -110,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             acc[m][r] = 0.f;
 
     struct Stage {
-        uint32_t w[NWG];
+        uint32_t w[WS ? 4 * NPC : NWG];
     };
     Stage ring[PD];
 
@@ -154,7 +174,19 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
         auto load = [&](Stage &st, int task) {
             const int r = task / SLOTS, sl = task % SLOTS;
             const uint32_t *wbase = slab.p.wq + rowbase[r] * wpr + (size_t)g0 * NWG;
-            load_words<NWG, ALIGN>(byte_offset(wbase, rowlane[r] + (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
+            if constexpr (WS) {
+                // piece lam + LPR j of the slot's span, clamped to the chunk's last 16 bytes
+                const uint32_t last = (uint32_t)(ng * GBY - 16);
+#pragma unroll
+                for (int j = 0; j < NPC; ++j) {
+                    const uint32_t off = min((uint32_t)(sl * LPR * GBY + 16 * (lam + LPR * j)), last);
+                    const u32x4 v = load_weight(reinterpret_cast<const u32x4 *>(
+                        byte_offset(wbase, rowlane[r] + off)));
+                    st.w[4 * j + 0] = v.x; st.w[4 * j + 1] = v.y; st.w[4 * j + 2] = v.z; st.w[4 * j + 3] = v.w;
+                }
+            } else {
+                load_words<NWG, ALIGN>(byte_offset(wbase, rowlane[r] + (uint32_t)(lgroup[sl] * NWG * 4)), st.w);
+            }
         };
 #pragma unroll
         for (int t = 0; t < PD; ++t)
@@ -225,8 +257,45 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
             const int r = t / SLOTS, sl = t % SLOTS;
             Stage &st = ring[t % PD];
 #pragma unroll
-            for (int j = 0; j < NWG; ++j)
+            for (int j = 0; j < (WS ? 4 * NPC : NWG); ++j)
                 pin_register(st.w[j]);
+            uint32_t gw[NWG];  // this lane's group words
+            if constexpr (WS) {
+                // pieces to the wave's region, then this lane's group back
+                uint8_t *region = reinterpret_cast<uint8_t *>(wst + (size_t)(wave * RPI + rho) * RUNITS);
+                wave_lds_sync();  // the previous task's reads of the region are done
+#pragma unroll
+                for (int j = 0; j < NPC; ++j) {
+                    const int q = lam + LPR * j;  // logical 16-byte piece of the span
+                    const int phys = GU ? q + (q / GU) * ((GU | 1) - GU) : q;
+                    *reinterpret_cast<u32x4 *>(region + 16 * phys) =
+                        u32x4{st.w[4 * j], st.w[4 * j + 1], st.w[4 * j + 2], st.w[4 * j + 3]};
+                }
+                wave_lds_sync();  // other lanes' pieces are read below
+                const int gi = min(lam + sl * LPR, ng - 1) - sl * LPR;  // group within the slot (clamped)
+                const uint8_t *src = region + (size_t)max(gi, 0) * GSTRIDE;
+                if constexpr (RALIGN >= 16 && NWG % 4 == 0) {
+#pragma unroll
+                    for (int k = 0; k < NWG / 4; ++k) {
+                        const u32x4 v = reinterpret_cast<const u32x4 *>(src)[k];
+                        gw[4 * k] = v.x; gw[4 * k + 1] = v.y; gw[4 * k + 2] = v.z; gw[4 * k + 3] = v.w;
+                    }
+                } else if constexpr (RALIGN >= 8 && NWG % 2 == 0) {
+#pragma unroll
+                    for (int k = 0; k < NWG / 2; ++k) {
+                        const u32x2 v = reinterpret_cast<const u32x2 *>(src)[k];
+                        gw[2 * k] = v.x; gw[2 * k + 1] = v.y;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NWG; ++k)
+                        gw[k] = reinterpret_cast<const uint32_t *>(src)[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < NWG; ++k)
+                    gw[k] = st.w[k];
+            }
             if (sl * LPR < ng) {
                 const int gl = lam + sl * LPR;
                 const int glc = min(gl, ng - 1);
@@ -245,11 +314,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const ProductArgs a)
                 half2_t q[NPAIR];
                 bf16x2_t qb[NPAIR];
                 if constexpr (BF16)
-                    unpack_pairs_bf16<BITS, G>(st.w, qb);
+                    unpack_pairs_bf16<BITS, G>(gw, qb);
                 else if constexpr (BITS == 4)
-                    unpack_pairs4_int<G>(st.w, q);
+                    unpack_pairs4_int<G>(gw, q);
                 else
-                    unpack_pairs<BITS, G>(st.w, q);
+                    unpack_pairs<BITS, G>(gw, q);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     // two accumulators for 4-bit codes (even and odd pairs, two
@@ -312,6 +381,22 @@ hipError_t launch_qmv_slots(const ProductArgs &a, hipStream_t stream)
 {
     const int rows_per_block = kWaves * RPW;
     const dim3 grid((a.N + rows_per_block - 1) / rows_per_block, 1, a.split);
+    // Coalesced loads of wide groups (40 bytes and more): one-row fp16 launches
+    // on 16-byte rows with few workgroups. Measured against the per-lane group
+    // loads (us, 5120 x 5120 at M = 1): 8-bit G64 9.5 vs 12.4, 6-bit G64 8.5 vs
+    // 9.2, 5-bit G64 8.4 vs 8.9, 8-bit G64 on 5120 x 1024 5.2 vs 6.0; with
+    // groups of 20 to 32 bytes, or on the 5120 x 17408 projection (2176
+    // workgroups), the staging costs about what it saves or more (5-bit G32
+    // 8.2 vs 7.6, 4-bit G64 7.4 vs 7.1, 8-bit G32 on 5120 x 17408 22.0 vs 21.5).
+    constexpr bool kWide = G * BITS / 8 >= 40 && MR == 1 && !BF16;
+    if constexpr (kWide) {
+        const long long wgs = (a.N + rows_per_block - 1) / rows_per_block;
+        if (a.split == 1 && ((long long)a.K * BITS) % 128 == 0 && wgs <= 4LL * device_cu_count()) {
+            hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS, MR, BF16, true>), grid, dim3(kThreads), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((qmv_kernel<BITS, G, LPR, SLOTS, RPW, PD_ROWS, MR, BF16>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

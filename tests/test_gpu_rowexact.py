@@ -11,7 +11,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("bits,G,K", [(4, 32, 5120), (4, 32, 416), (5, 64, 2560), (6, 32, 1280),
-                                      (8, 128, 2048), (4, 32, 17408), (4, 64, 8192)])
+                                      (8, 128, 2048), (4, 32, 17408), (4, 64, 8192),
+                                      # groups of 40+ bytes: the one-row launch loads them coalesced
+                                      # through LDS (several K chunks; 9280 x 5 bits leaves rows not
+                                      # 16-byte aligned, which takes the per-lane loads)
+                                      (8, 64, 17408), (6, 128, 8448), (5, 64, 9280)])
 @pytest.mark.parametrize("M", [2, 3, 5, 8, 11])
 def test_rows_bitwise_equal_one_row_calls(bits, G, K, M):
     N = 150
