@@ -109,6 +109,7 @@ hipError_t launch_compare_words(const uint32_t *a, const uint32_t *b, size_t cou
                                 hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size_t count,
                                 hipStream_t stream);
+hipError_t launch_zero(float *y, size_t count, hipStream_t stream);  // y[0 .. count) = 0
 
 // Group range [begin, end) of K slice z when Kg groups are split into S
 // slices: floor(Kg/S) groups each, one more for the first Kg mod S slices.

@@ -101,6 +101,7 @@ struct XrArgs {
     int npass;   // K passes: wave kp owns parts kp, KP + kp, 2 KP + kp, ... of the slice
     int batch;   // tiles whose partial sums are reduced after one barrier
     int nbuf;    // partial-sum buffers: 1 when one batch holds every tile of a workgroup's one pass, else 2
+    int add;     // the two K slices (grid z) add into a zeroed y instead of writing partials
 };
 
 // Group range [pb, pe) of part kp: the slice [gb, ge) cut into KP parts of
@@ -554,8 +555,12 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                             continue;
                         }
                     }
-                    if (col < N && m < M)
-                        yout[(size_t)m * N + col] = o;
+                    if (col < N && m < M) {
+                        if (xa.add)  // exactly two addends on +0: the same sum in either order
+                            atomicAdd(&yout[(size_t)m * N + col], o);
+                        else
+                            yout[(size_t)m * N + col] = o;
+                    }
                 }
             }
         }
@@ -715,12 +720,12 @@ template <int BITS>
 constexpr int xr_pass_codes() { return XR_MP_WIDE && BITS <= 4 ? xr_large_codes<BITS>() : xr_small_codes<BITS>(); }
 
 template <int BITS, int G, int XC, bool BF16>
-hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream)
+hipError_t launch_xr_variant(const ProductArgs &a, const XrPlan &plan, hipStream_t stream, bool add = false)
 {
     XrShape sh;
     if (!xr_shape<BITS, G, XC>(a, plan.KP, plan.npass, xr_grid_x(a, plan.KP, plan.npass), sh))
         return hipErrorInvalidValue;  // excluded by plan_xr
-    XrArgs xa{a, plan.gran, (a.N + 15) / 16, plan.npass, sh.batch, sh.nbuf};
+    XrArgs xa{a, plan.gran, (a.N + 15) / 16, plan.npass, sh.batch, sh.nbuf, add ? 1 : 0};
     const dim3 grid(sh.gx, 1, a.split), block(plan.KP * kWave);
     const size_t lds = sh.lds;
     constexpr int NST4 = xr_stages_sbw(BITS, XC, 4), NST2 = xr_stages_sbw(BITS, XC, 2);
@@ -807,6 +812,29 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
     done = plan_xr_any<BITS, G>(a, plan, xc);
     if (!done)
         return hipSuccess;
+    // Long K in one slice (several passes per wave): two half-K slices on twice
+    // the workgroups, each adding its tiles into y (zeroed first). Exactly two
+    // addends reach each output, so the result does not depend on their order.
+    if (plan.npass > 1 && a.split == 1) {
+        ProductArgs h = a;
+        h.split = 2;
+        h.y_slice_stride = 0;
+        XrPlan hp;
+        int hxc = 0;
+        if (plan_xr_any<BITS, G>(h, hp, hxc)) {
+            for (int j = 0; j < (a.nproj >= 2 ? a.nproj : 1); ++j) {
+                const Proj &pj = a.nproj >= 2 ? a.proj[j] : Proj{a.wq, a.scales, a.biases, a.y, a.N};
+                const hipError_t e = launch_zero(pj.y, (size_t)a.M * pj.N, stream);
+                if (e != hipSuccess)
+                    return e;
+            }
+            if (hxc == xr_small_codes<BITS>())
+                return launch_xr_variant<BITS, G, xr_small_codes<BITS>(), BF16>(h, hp, stream, true);
+            if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>())
+                return launch_xr_variant<BITS, G, xr_large_codes<BITS>(), BF16>(h, hp, stream, true);
+            return hipErrorInvalidValue;
+        }
+    }
     if (xc == xr_small_codes<BITS>())
         return launch_xr_variant<BITS, G, xr_small_codes<BITS>(), BF16>(a, plan, stream);
     if constexpr (xr_large_codes<BITS>() != xr_small_codes<BITS>())

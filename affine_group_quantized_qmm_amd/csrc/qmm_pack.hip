@@ -46,6 +46,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
+// y[i] = 0 for i < count (the launches that add two K halves into y start
+// from it; a kernel rather than a memset, so that graph replays stay exact).
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ y, size_t count)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+        y[i] = 0.f;
+}
+
 // Number of positions i < count where the 32-bit words a[i] and b[i]
 // differ, written to *mismatches by one workgroup (no atomics, no clearing).
 __global__ __launch_bounds__(256) void compare_words_kernel(const uint32_t *__restrict__ a,
@@ -95,6 +103,12 @@ hipError_t launch_splitk_reduce(const float *partials, float *y, int split, size
 {
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(count, 256)), dim3(256), 0, stream,
                        partials, y, split, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(float *y, size_t count, hipStream_t stream)
+{
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_for(count, 256)), dim3(256), 0, stream, y, count);
     return hipGetLastError();
 }
 

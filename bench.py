@@ -98,6 +98,7 @@ KERNEL_SOURCES = {
 # rocprofv3 kernel-name fragments of the library's kernels
 KERNEL_SYMBOLS = {"mfma": "mfma_xr_kernel", "mfma_lds": "mfma_kernel<", "qmv": "qmv_kernel",
                   "reduce": "splitk_reduce_kernel", "read": "stream_read_kernel"}
+ZERO_SYMBOL = "zero_kernel"  # clears y for the long-K launches
 PROFILES = ROOT / "profiles"
 PMC_SUMMARY = PROFILES / "dense_up_w4g32_hbm_traffic.txt"
 COPY_ELEMS = 64 * 2 ** 20  # fp32 elements of the calibration copy (256 MiB read, 256 MiB written)
@@ -186,8 +187,17 @@ def _per_dispatch(directory: str, counter: str):
 def _split_library(seq, manifest):
     """Library dispatches matched to the manifest's labels, and the copy
     calibration (the last PROFILE_REPS non-library dispatches; the first of
-    them, on cold caches, is dropped)."""
-    ours = [(n, v) for _, n, v in seq if "qmm::" in n]
+    them, on cold caches, is dropped). The fill that clears y ahead of a
+    long-K launch (its two K halves add into y) is counted with that launch."""
+    ours, pending = [], 0
+    for _, n, v in seq:
+        if "qmm::" not in n:
+            continue
+        if ZERO_SYMBOL in n:
+            pending += v
+            continue
+        ours.append((n, v + pending))
+        pending = 0
     other = [(n, v) for _, n, v in seq if "qmm::" not in n]
     labels = manifest["dispatches"]
     if len(ours) != len(labels):

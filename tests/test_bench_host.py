@@ -136,3 +136,17 @@ def test_counter_summary_averages_warm_rounds(tmp_path):
     text = written[0].read_text()
     assert written[0].name == "dense_up_w4g32_sq_counters.txt"
     assert "M1 | qmv | 100" in text and "M4 | mfma | 400" in text and "M16 | mfma | 1600" in text
+
+
+def test_y_fill_counted_with_the_long_k_launch():
+    """The fill that clears y ahead of a long-K launch carries no manifest
+    label of its own: its counts are added to the launch that follows it."""
+    mfma = "void qmm::(anonymous namespace)::mfma_xr_kernel<4>(x)"
+    fill = "qmm::(anonymous namespace)::zero_kernel(float*, unsigned long)"
+    seq = [(0, "void at::native::upload(x)", 5.0), (1, fill, 2.0), (2, mfma, 30.0), (3, mfma, 20.0),
+           (4, "void at::native::copy(x)", 7.0)]
+    labels = [{"set": "longk", "label": "S1", "round": 0, "algorithmic_bytes": 1},
+              {"set": "headline", "label": "M4", "round": 0, "algorithmic_bytes": 1}]
+    pairs, other = bench._split_library(seq, {"dispatches": labels})
+    assert [(lab["label"], v) for lab, (_, v) in pairs] == [("S1", 32.0), ("M4", 20.0)]
+    assert all("zero_kernel" not in n for _, (n, _) in pairs)

@@ -131,6 +131,26 @@ def test_deterministic_rerun():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("bits,G", [(4, 32), (8, 64), (3, 32)])
+def test_long_k_two_halves(bits, G):
+    """K too long for one pass of the matrix-core kernel: the two K halves add
+    into y, which the call clears first (y starts as NaN here). Two addends
+    per output, so reruns are bitwise identical; parity with the oracle."""
+    K, N, M = 17408, 336, 5
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=23, M=M, K=K, N=N, bits=bits, G=G))
+    qmm = _gpu.lib()
+    assert qmm.qmm_kernel_name(M, K, N, bits, G) == "mfma"
+    outs = []
+    for _ in range(4):
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dp.x.device)
+        outs.append(qmm.qmm_forward(dp.x, dp.wq, dp.s, dp.b, bits, G, out=y))
+    torch.cuda.synchronize()
+    ref, absum = dp.oracle()
+    _gpu.assert_parity(outs[0], ref, absum, f"long K bits={bits} G={G}")
+    for y in outs[1:]:
+        assert torch.equal(y, outs[0])
+
+
 def test_rejects_misaligned_tensor():
     qmm = _gpu.lib()
     bits, G, K, N = 4, 32, 256, 64
