@@ -131,12 +131,14 @@ def test_deterministic_rerun():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("bits,G", [(4, 32), (8, 64), (3, 32)])
-def test_long_k_two_halves(bits, G):
-    """K too long for one pass of the matrix-core kernel: the two K halves add
-    into y, which the call clears first (y starts as NaN here). Two addends
-    per output, so reruns are bitwise identical; parity with the oracle."""
-    K, N, M = 17408, 336, 5
+@pytest.mark.parametrize("bits,G,K,N,M", [(4, 32, 17408, 336, 5), (8, 64, 17408, 336, 5), (3, 32, 17408, 336, 5),
+                                          (4, 32, 6176, 1, 3), (4, 32, 6176, 17, 16), (5, 64, 6272, 40, 8),
+                                          (2, 32, 12288, 50, 4)])
+def test_long_k_two_halves(bits, G, K, N, M):
+    """K too long for one pass of the matrix-core kernel (from just past the
+    one-pass limit on): the two K halves add into y, which the call clears
+    first (y starts as NaN here). Two addends per output, so reruns are
+    bitwise identical; parity with the oracle; N down to one column."""
     dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=23, M=M, K=K, N=N, bits=bits, G=G))
     qmm = _gpu.lib()
     assert qmm.qmm_kernel_name(M, K, N, bits, G) == "mfma"
