@@ -52,9 +52,10 @@ constexpr size_t kXrLdsLimit = 160 * 1024;  // LDS of one CU
 constexpr int kXrMaxPasses = XR_MAX_PASSES;  // K parts per wave (activations reloaded between them)
 constexpr int kXrBatchMax = 6;    // tiles whose partial sums are reduced after one barrier, at most
 
-// Activations per row held by one wave (XC: 640 or 768, 512 for 8-bit codes,
-// i.e. 80 to 96 registers of A operands). The host takes the first variant
-// of a width whose parts fit the workgroup (xr_variants).
+// Activations per row held by one wave (XC: 640 or 768, i.e. 80 or 96
+// registers of A operands; 640 for 8-bit codes, and 512 in the tiled
+// layout's 8-bit variant). The host takes the first variant of a width whose
+// parts fit the workgroup (plan_xr_any).
 //
 // Tiles of loads in flight per wave (register stages): one. A stage's
 // registers are free again as soon as its tile is in LDS, so the next
