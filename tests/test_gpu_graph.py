@@ -101,3 +101,18 @@ def test_graph_replays_of_the_other_entry_points(M):
     yt = torch.empty((M, N), dtype=torch.float32, device=dev)
     (yt_e,) = _replays_equal_eager(lambda: qmm.qmm_forward_tiled(dp.x, tw, tsb, N, bits, G, out=yt), [yt], "tiled")
     _gpu.assert_parity(yt_e, ref, absum, f"graph tiled M={M}")
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_graph_replays_of_the_long_k_launch(M):
+    """K past the one-pass limit: the fill that clears y and the two K halves
+    adding into it, captured together; every replay (y NaN-filled before it)
+    equals the eager call bit for bit."""
+    bits, G, K, N = 4, 32, 12288, 200
+    qmm = _gpu.lib()
+    dp = _gpu.DeviceProblem(qmm_inputs.make_problem(seed=90 + M, M=M, K=K, N=N, bits=bits, G=G))
+    assert qmm.qmm_kernel_name(M, K, N, bits, G) == "mfma"
+    y = torch.empty((M, N), dtype=torch.float32, device=dp.x.device)
+    (ye,) = _replays_equal_eager(lambda: qmm.qmm_forward(dp.x, dp.wq, dp.s, dp.b, bits, G, out=y), [y], "long K")
+    ref, absum = dp.oracle()
+    _gpu.assert_parity(ye, ref, absum, f"graph long K M={M}")
