@@ -107,13 +107,13 @@ struct XrArgs {
 
 // Group range [pb, pe) of part kp: the slice [gb, ge) cut into KP parts of
 // whole granules of `gran` groups (the last granule may be short).
-__device__ __forceinline__ void part_range(int gb, int ge, int KP, int kp, int gran, int &pb, int &pe)
+__host__ __device__ inline void part_range(int gb, int ge, int KP, int kp, int gran, int &pb, int &pe)
 {
     const int nu = (ge - gb + gran - 1) / gran;
     int ub, ue;
     slice_groups(nu, KP, kp, ub, ue);
-    pb = min(gb + ub * gran, ge);
-    pe = min(gb + ue * gran, ge);
+    pb = gb + ub * gran < ge ? gb + ub * gran : ge;
+    pe = gb + ue * gran < ge ? gb + ue * gran : ge;
 }
 
 // Dynamic LDS of one workgroup of KP waves: per wave a weight tile region
@@ -541,11 +541,25 @@ __global__ __launch_bounds__(kXrMaxParts *kWave) void mfma_xr_kernel(const XrArg
                 float *__restrict__ yout = ts.p.y + (size_t)blockIdx.z * a.y_slice_stride;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = red_at(buf, sl, 0, r);
-                    for (int p = 1; p < KP; ++p)
-                        v += red_at(buf, sl, p, r);
+                    float o;
+                    if (!MP && !xa.add && KP % 2 == 0) {
+                        // the two halves of the parts summed apart and then
+                        // added: the bits of an additive two-slice launch over
+                        // the same parts, (0 + a) + b (kOutScale is a power of
+                        // two, so the products are exact)
+                        float va = red_at(buf, sl, 0, r), vb = red_at(buf, sl, KP / 2, r);
+                        for (int p = 1; p < KP / 2; ++p) {
+                            va += red_at(buf, sl, p, r);
+                            vb += red_at(buf, sl, KP / 2 + p, r);
+                        }
+                        o = va * kOutScale + vb * kOutScale;
+                    } else {
+                        float v = red_at(buf, sl, 0, r);
+                        for (int p = 1; p < KP; ++p)
+                            v += red_at(buf, sl, p, r);
+                        o = v * kOutScale;
+                    }
                     const int m = 4 * c + r;
-                    float o = v * kOutScale;
                     if constexpr (MP) {
                         // the running sum of the earlier passes, kept by this thread
                         float &run = accl[((size_t)(first + sl - t0) * 4 + r) * kWave + lane];
@@ -805,6 +819,30 @@ bool plan_xr_any(const ProductArgs &a, XrPlan &plan, int &xc)
     return false;
 }
 
+// Whether a one-pass, one-slice plan and a one-pass, two-slice plan of the
+// same variant cut K into the same parts (slice z's parts being parts
+// z*KP/2 .. z*KP/2 + KP/2 - 1 of the one slice).
+template <int G>
+bool xr_same_parts(const ProductArgs &a, const XrPlan &one, int xc1, const XrPlan &two, int xc2)
+{
+    if (xc1 != xc2 || one.npass != 1 || two.npass != 1 || one.KP != 2 * two.KP || one.gran != two.gran ||
+        one.sbw != two.sbw)
+        return false;
+    const int Kg = a.K / G;
+    for (int z = 0; z < 2; ++z) {
+        int gb, ge;
+        slice_groups(Kg, 2, z, gb, ge);
+        for (int kp = 0; kp < two.KP; ++kp) {
+            int b1, e1, b2, e2;
+            part_range(0, Kg, one.KP, z * two.KP + kp, one.gran, b1, e1);
+            part_range(gb, ge, two.KP, kp, two.gran, b2, e2);
+            if (b1 != b2 || e1 != e2)
+                return false;
+        }
+    }
+    return true;
+}
+
 template <int BITS, int G, bool BF16>
 hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
 {
@@ -813,16 +851,26 @@ hipError_t launch_xr_t(const ProductArgs &a, hipStream_t stream, bool &done)
     done = plan_xr_any<BITS, G>(a, plan, xc);
     if (!done)
         return hipSuccess;
-    // Long K in one slice (several passes per wave): two half-K slices on twice
-    // the workgroups, each adding its tiles into y (zeroed first). Exactly two
-    // addends reach each output, so the result does not depend on their order.
-    if (plan.npass > 1 && a.split == 1) {
+    // Two half-K slices on twice the workgroups, each adding its tiles into y
+    // (zeroed first); exactly two addends reach each output, so the result
+    // does not depend on their order.
+    //  * Long K (several passes per wave in one slice): 26.6 against 30.2 us
+    //    on the 17408 x 5120 4-bit projection at M = 16.
+    //  * Small N, when the one-slice grid leaves at least half the CUs idle:
+    //    the halves' workgroups still get a CU each and every chain is half as
+    //    long (8.7 against 9.5 us at N = 1024 and K = 5120, 9.3 against 10.4
+    //    for 8-bit G64 codes at N = 2048; M = 16). Taken only where the halves
+    //    cut K into the one-slice launch's parts, whose epilogue sums the two
+    //    halves of its parts apart: both launches then give the same bits,
+    //    so fused and separate calls agree whichever of the two they take.
+    const bool small_n = plan.npass == 1 && plan.KP % 2 == 0 && 2 * xr_grid_x(a, plan.KP, 1) <= device_cu_count();
+    if ((plan.npass > 1 || small_n) && a.split == 1) {
         ProductArgs h = a;
         h.split = 2;
         h.y_slice_stride = 0;
         XrPlan hp;
         int hxc = 0;
-        if (plan_xr_any<BITS, G>(h, hp, hxc)) {
+        if (plan_xr_any<BITS, G>(h, hp, hxc) && (plan.npass > 1 || xr_same_parts<G>(a, plan, xc, hp, hxc))) {
             for (int j = 0; j < (a.nproj >= 2 ? a.nproj : 1); ++j) {
                 const Proj &pj = a.nproj >= 2 ? a.proj[j] : Proj{a.wq, a.scales, a.biases, a.y, a.N};
                 const hipError_t e = launch_zero(pj.y, (size_t)a.M * pj.N, stream);

@@ -111,10 +111,12 @@ int qmm_pack(const uint8_t *codes, uint32_t *packed, int N, int K, int bits,
  * request #565 page, tiling-policy commit, routes fewer than four rows to
  * the one-row mat-vec because it is faster there; here the matrix cores win
  * from three rows on). When K is too long for one pass of the matrix-core
- * kernel, a first launch clears y and the two K halves then add into it
- * with fp32 atomics: each output receives exactly two addends on +0, and
- * their sum does not depend on arrival order, so reruns stay bitwise
- * identical. y must not alias the inputs.
+ * kernel, or N so small that one launch would leave half the CUs idle, a
+ * first launch clears y and the two K halves then add into it with fp32
+ * atomics: each output receives exactly two addends on +0, and their sum
+ * does not depend on arrival order, so reruns stay bitwise identical (for
+ * small N the halves are used only where they give the bits of the one-slice
+ * launch). y must not alias the inputs.
  */
 int qmm_forward(const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
                 const uint16_t *biases, float *y, int M, int K, int N, int bits, int G,

@@ -29,6 +29,9 @@ def make_projections(seed, M, K, Ns, bits, G):
     (4, 32, 17408, [33, 20]),             # several K parts per wave
     (4, 32, 65536, [33, 20]),             # more than 8 passes: LDS kernel
     (5, 32, 416, [40, 9]),                # rows not whole 16-byte units: LDS kernel
+    (4, 32, 5120, [5120, 1024]),          # alone, the small projection runs as two additive K halves;
+    (8, 64, 5120, [2048, 4096]),          # fused, the launch is one slice: the same bits either way
+    (4, 32, 5216, [4096, 40]),            # ragged parts: halves only where they match the one-slice parts
 ])
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 16, 19])
 def test_fused_equals_separate_calls(bits, G, K, Ns, M):
